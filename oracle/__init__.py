@@ -1,0 +1,71 @@
+"""CPU oracle for column-wise top-k -- test infrastructure only.
+
+Only tests/, the smoke check in __graft_entry__ and bench.py's CPU-baseline
+leg import this package.  The GPU path never imports it and it imports
+nothing from the GPU path.
+
+`topk_cols` wraps the plain-C oracle in topk_oracle.c (a full qsort of every
+column under the order "larger value first, ties to the smaller row id"; see
+that file's header for the readings of -0, NaN and the emitted bits).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+BF16 = 0
+F32 = 1
+COL_CONTIG = 0
+ROW_INTERLEAVED = 1
+
+_lib = None
+
+
+def load_library(path):
+    """Load an oracle build (the default one, or a test's planted-mistake build)."""
+    lib = ctypes.CDLL(path)
+    lib.oracle_topk_cols.restype = ctypes.c_int
+    lib.oracle_topk_cols.argtypes = [
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        path = _build.LIBRARY
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SOURCE):
+            _build.build()
+        _lib = load_library(path)
+    return _lib
+
+
+def topk_cols(x, V, C, k, dtype, layout, ld, nthreads=1, lib=None):
+    """Top-k of every column of the V x C matrix stored in `x`.
+
+    x: a contiguous numpy array holding the raw storage (np.uint16 bit
+       patterns for bf16, np.float32 or np.uint32 for fp32), element (r, c) at
+       x.flat[c*ld + r] (column-contiguous) or x.flat[r*ld + c] (interleaved).
+    Returns (values, ids): values has the storage dtype of x, shape (C, k),
+    bit-copied from x; ids is int32 (C, k).  Entry [c, 0] is the largest.
+    nthreads: worker threads, split over columns.  lib: an alternative build
+    returned by load_library (default: oracle/liboracle_topk.so).
+    """
+    x = np.ascontiguousarray(x)
+    if dtype == BF16 and x.dtype != np.uint16:
+        raise TypeError("bf16 input must be given as np.uint16 bit patterns")
+    if dtype == F32 and x.dtype not in (np.float32, np.uint32):
+        raise TypeError("fp32 input must be np.float32 or np.uint32")
+    need = (C - 1) * ld + V if layout == COL_CONTIG else (V - 1) * ld + C
+    if x.size < need:
+        raise ValueError(f"x holds {x.size} elements, the layout needs {need}")
+    values = np.empty((C, k), dtype=x.dtype)
+    ids = np.empty((C, k), dtype=np.int32)
+    rc = (lib or _load()).oracle_topk_cols(V, C, k, dtype, layout, ld, x.ctypes.data,
+                                  values.ctypes.data, ids.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_topk_cols failed with status {rc}")
+    return values, ids
