@@ -1,0 +1,61 @@
+"""Builds libtopk_cols.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
+
+    python -m drafter_vocab_top_amd.build
+
+The library is placed next to this file; the Python binding loads it from
+there.  hipcc cross-compiles for gfx950 without a GPU.
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIBRARY = os.path.join(HERE, "libtopk_cols.so")
+SOURCES = [os.path.join(CSRC, n) for n in ("topk_col.hip", "topk_cols_api.cpp")]
+HEADERS = [os.path.join(CSRC, n) for n in ("topk_device.hpp", "topk_internal.hpp")] + \
+          [os.path.join(INCLUDE, "topk_cols.h")]
+ARCH = "gfx950"
+
+
+def hipcc():
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    path = os.path.join(rocm, "bin", "hipcc")
+    return path if os.path.exists(path) else "hipcc"
+
+
+def command(output=LIBRARY):
+    return [hipcc(), "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
+            # keep the compiler from emitting packed fp32 instructions
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wall", "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC,
+            "-o", output] + SOURCES
+
+
+def build(verbose=False):
+    tmp = LIBRARY + ".tmp"
+    cmd = command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+    os.replace(tmp, LIBRARY)
+    return LIBRARY
+
+
+def stale():
+    if not os.path.exists(LIBRARY):
+        return True
+    t = os.path.getmtime(LIBRARY)
+    return any(os.path.getmtime(p) > t for p in SOURCES + HEADERS)
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,176 @@
+// C ABI of the column-wise top-k library (declared in include/topk_cols.h):
+// argument checks, workspace ownership, launch decomposition and dispatch to
+// the kernels.  No function here synchronizes the device except create and
+// destroy, and no function aborts.
+#include "topk_cols.h"
+
+#include <stdlib.h>
+
+#include <new>
+
+#include "topk_internal.hpp"
+
+struct topk_cols {
+    int64_t V, C, ld;
+    int32_t k;
+    int32_t dtype, layout;
+    int device;
+    int64_t segments;   // workgroups per column
+    int64_t blocks;     // workgroups of the main kernel
+    void* workspace;    // tickets then partial keys
+    size_t workspace_bytes;
+    uint32_t* tickets;
+    uint64_t* partials;
+    uint32_t runs;      // completed run() calls, for the run tag
+};
+
+namespace {
+
+constexpr int64_t kBlockThreads = 256;
+// A single pass holds this many 16-byte vectors per workgroup.
+constexpr int64_t kVecsPerPass = kBlockThreads * topk::kColVecsPerThread;
+// Workgroups the column-contiguous launch aims for: enough that every CU has
+// work even when the matrix has few columns.
+constexpr int64_t kTargetBlocksPerCU = 2;
+// Do not split a column into segments smaller than this many vectors.
+constexpr int64_t kMinVecsPerSegment = 64;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int element_size(int32_t dtype) { return dtype == TOPK_BF16 ? 2 : 4; }
+
+int64_t choose_col_segments(int64_t V, int64_t C, int32_t k, int dtype, int cu_count) {
+    const int64_t per_vec = 16 / element_size(dtype);
+    const int64_t nvec = V / per_vec;
+    int64_t s = ceil_div(nvec, kVecsPerPass);                          // one pass per workgroup
+    const int64_t fill = ceil_div((int64_t)cu_count * kTargetBlocksPerCU, C);
+    if (fill > s) s = fill;
+    const int64_t most = nvec / kMinVecsPerSegment;                    // not too thin
+    if (s > most) s = most;
+    const int64_t merge_cap = topk::kMaxMergeKeys / k;
+    if (s > merge_cap) s = merge_cap;
+    return s < 1 ? 1 : s;
+}
+
+int create_impl(topk_cols_t* out, int64_t V, int64_t C, int32_t k, int32_t dtype, int32_t layout,
+                int64_t ld, int64_t forced_segments) {
+    if (!out) return TOPK_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (V < 1 || C < 1 || k < 1 || (int64_t)k > V) return TOPK_ERR_INVALID_ARG;
+    if (dtype != TOPK_BF16 && dtype != TOPK_F32) return TOPK_ERR_INVALID_ARG;
+    if (layout != TOPK_COL_CONTIG && layout != TOPK_ROW_INTERLEAVED) return TOPK_ERR_INVALID_ARG;
+    if (layout == TOPK_COL_CONTIG && ld < V) return TOPK_ERR_INVALID_ARG;
+    if (layout == TOPK_ROW_INTERLEAVED && ld < C) return TOPK_ERR_INVALID_ARG;
+    if (forced_segments < 0) return TOPK_ERR_INVALID_ARG;
+    if (k > TOPK_MAX_K || V > TOPK_MAX_V) return TOPK_ERR_UNSUPPORTED;
+    if (layout == TOPK_ROW_INTERLEAVED) return TOPK_ERR_UNSUPPORTED;
+    if (forced_segments > 0 && forced_segments * k > topk::kMaxMergeKeys) return TOPK_ERR_UNSUPPORTED;
+
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return TOPK_ERR_HIP;
+    int cu_count = 0;
+    if (hipDeviceGetAttribute(&cu_count, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+        cu_count < 1)
+        return TOPK_ERR_HIP;
+
+    const int64_t S = forced_segments > 0 ? forced_segments
+                                          : choose_col_segments(V, C, k, dtype, cu_count);
+    const int64_t blocks = C * S;
+    if (blocks > 0x7FFFFFFF) return TOPK_ERR_UNSUPPORTED;
+
+    const size_t ticket_bytes = ((size_t)C * sizeof(uint32_t) + 255) & ~(size_t)255;
+    const size_t partial_bytes = S > 1 ? (size_t)C * (size_t)S * (size_t)k * sizeof(uint64_t) : 0;
+    const size_t ws_bytes = ticket_bytes + partial_bytes;
+
+    topk_cols* h = new (std::nothrow) topk_cols();
+    if (!h) return TOPK_ERR_OUT_OF_MEMORY;
+    h->V = V; h->C = C; h->ld = ld; h->k = k; h->dtype = dtype; h->layout = layout;
+    h->device = device; h->segments = S; h->blocks = blocks;
+    h->workspace_bytes = ws_bytes;
+    hipError_t e = hipMalloc(&h->workspace, ws_bytes);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        delete h;
+        return e == hipErrorOutOfMemory ? TOPK_ERR_OUT_OF_MEMORY : TOPK_ERR_HIP;
+    }
+    h->tickets = static_cast<uint32_t*>(h->workspace);
+    h->partials = S > 1 ? reinterpret_cast<uint64_t*>(static_cast<char*>(h->workspace) + ticket_bytes)
+                        : nullptr;
+    if (hipMemset(h->workspace, 0, ws_bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        (void)hipFree(h->workspace);
+        delete h;
+        return TOPK_ERR_HIP;
+    }
+    *out = h;
+    return TOPK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int topk_cols_create(topk_cols_t* out, int64_t V, int64_t C, int32_t k, int32_t dtype,
+                     int32_t layout, int64_t ld) {
+    return create_impl(out, V, C, k, dtype, layout, ld, 0);
+}
+
+int topk_cols_create_with_segments(topk_cols_t* out, int64_t V, int64_t C, int32_t k,
+                                   int32_t dtype, int32_t layout, int64_t ld, int64_t segments) {
+    return create_impl(out, V, C, k, dtype, layout, ld, segments);
+}
+
+int topk_cols_run(topk_cols_t h, const void* logits, void* out_values, int32_t* out_ids,
+                  hipStream_t stream) {
+    if (!h || !logits || !out_values || !out_ids) return TOPK_ERR_INVALID_ARG;
+    const uintptr_t es = (uintptr_t)element_size(h->dtype);
+    if (((uintptr_t)logits % es) != 0 || ((uintptr_t)out_values % es) != 0 ||
+        ((uintptr_t)out_ids % 4) != 0)
+        return TOPK_ERR_INVALID_ARG;
+
+    topk::ColArgs a;
+    a.x = logits;
+    a.ld = h->ld;
+    a.V = h->V;
+    a.C = (int32_t)h->C;
+    a.k = h->k;
+    a.S = (int32_t)h->segments;
+    a.tag = 1u + (h->runs % 255u);
+    a.partials = h->partials;
+    a.tickets = h->tickets;
+    a.out_values = out_values;
+    a.out_ids = out_ids;
+    const hipError_t e = h->dtype == TOPK_BF16 ? topk::launch_col_bf16(a, stream)
+                                               : topk::launch_col_f32(a, stream);
+    if (e != hipSuccess) return TOPK_ERR_HIP;
+    ++h->runs;
+    return TOPK_OK;
+}
+
+int topk_cols_destroy(topk_cols_t h) {
+    if (!h) return TOPK_OK;
+    int status = TOPK_OK;
+    if (h->workspace && hipFree(h->workspace) != hipSuccess) status = TOPK_ERR_HIP;
+    delete h;
+    return status;
+}
+
+const char* topk_cols_status_string(int status) {
+    switch (status) {
+        case TOPK_OK: return "TOPK_OK";
+        case TOPK_ERR_INVALID_ARG: return "TOPK_ERR_INVALID_ARG: an argument is out of range, NULL or misaligned";
+        case TOPK_ERR_UNSUPPORTED: return "TOPK_ERR_UNSUPPORTED: valid, but beyond this build's limits";
+        case TOPK_ERR_HIP: return "TOPK_ERR_HIP: a HIP runtime call failed";
+        case TOPK_ERR_OUT_OF_MEMORY: return "TOPK_ERR_OUT_OF_MEMORY: the workspace could not be allocated";
+        default: return "unknown topk_cols status";
+    }
+}
+
+int topk_cols_query(topk_cols_t h, int64_t* segments, int64_t* blocks, int64_t* workspace_bytes) {
+    if (!h) return TOPK_ERR_INVALID_ARG;
+    if (segments) *segments = h->segments;
+    if (blocks) *blocks = h->blocks;
+    if (workspace_bytes) *workspace_bytes = (int64_t)h->workspace_bytes;
+    return TOPK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,160 @@
+"""ctypes binding of libtopk_cols.so, the HIP column-wise top-k library.
+
+The binding only marshals arguments.  It passes raw device pointers and the
+current HIP stream to the C ABI in include/topk_cols.h; every step of the
+selection runs in the library's kernels.  PyTorch supplies the device buffers
+and the stream.
+
+    h = TopkCols(V, C, k, "bf16", "col", ld)
+    values, ids = h.run(x)            # x: torch tensor on the GPU
+    h.close()
+
+Loading fails loudly when the library is missing or cannot be loaded.  There
+is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtopk_cols.so")
+
+TOPK_OK = 0
+TOPK_ERR_INVALID_ARG = -1
+TOPK_ERR_UNSUPPORTED = -2
+TOPK_ERR_HIP = -3
+TOPK_ERR_OUT_OF_MEMORY = -4
+TOPK_MAX_K = 64
+TOPK_MAX_V = (1 << 24) - 1
+
+DTYPES = {"bf16": 0, "f32": 1}
+LAYOUTS = {"col": 0, "row": 1}
+
+EXPORTED = ("topk_cols_create", "topk_cols_create_with_segments", "topk_cols_run",
+            "topk_cols_destroy", "topk_cols_status_string", "topk_cols_query")
+
+_lib = None
+
+
+class TopkError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)}")
+
+
+def load(path: str = LIBRARY):
+    """Load the library (once) and declare its C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise OSError(f"{path} is missing: build it with `python -m drafter_vocab_top_amd.build`")
+    lib = ctypes.CDLL(path)
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.topk_cols_create.argtypes = [ctypes.POINTER(p), i64, i64, i32, i32, i32, i64]
+    lib.topk_cols_create.restype = ctypes.c_int
+    lib.topk_cols_create_with_segments.argtypes = [ctypes.POINTER(p), i64, i64, i32, i32, i32, i64, i64]
+    lib.topk_cols_create_with_segments.restype = ctypes.c_int
+    lib.topk_cols_run.argtypes = [p, p, p, p, p]
+    lib.topk_cols_run.restype = ctypes.c_int
+    lib.topk_cols_destroy.argtypes = [p]
+    lib.topk_cols_destroy.restype = ctypes.c_int
+    lib.topk_cols_status_string.argtypes = [ctypes.c_int]
+    lib.topk_cols_status_string.restype = ctypes.c_char_p
+    lib.topk_cols_query.argtypes = [p, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.topk_cols_query.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().topk_cols_status_string(int(status)).decode()
+
+
+def _torch_dtype(dtype: str):
+    import torch
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+class TopkCols:
+    """One top-k shape on the current GPU (a handle of the C library)."""
+
+    def __init__(self, V: int, C: int, k: int, dtype: str = "bf16", layout: str = "col",
+                 ld: int | None = None, segments: int = 0):
+        if dtype not in DTYPES or layout not in LAYOUTS:
+            raise ValueError(f"dtype must be one of {list(DTYPES)}, layout one of {list(LAYOUTS)}")
+        self.V, self.C, self.k, self.dtype, self.layout = V, C, k, dtype, layout
+        self.ld = ld if ld is not None else (V if layout == "col" else C)
+        lib = load()
+        self._h = ctypes.c_void_p()
+        rc = lib.topk_cols_create_with_segments(ctypes.byref(self._h), V, C, k, DTYPES[dtype],
+                                                LAYOUTS[layout], self.ld, segments)
+        if rc != TOPK_OK:
+            raise TopkError(rc, "topk_cols_create")
+
+    def query(self) -> dict:
+        s, b, w = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        rc = load().topk_cols_query(self._h, ctypes.byref(s), ctypes.byref(b), ctypes.byref(w))
+        if rc != TOPK_OK:
+            raise TopkError(rc, "topk_cols_query")
+        return {"segments": s.value, "blocks": b.value, "workspace_bytes": w.value}
+
+    def run_ptr(self, x_ptr: int, values_ptr: int, ids_ptr: int, stream_ptr: int) -> None:
+        """Enqueue one run on raw device pointers and a raw HIP stream handle."""
+        rc = load().topk_cols_run(self._h, x_ptr, values_ptr, ids_ptr, stream_ptr)
+        if rc != TOPK_OK:
+            raise TopkError(rc, "topk_cols_run")
+
+    def run(self, x, values=None, ids=None, stream=None):
+        """Enqueue one run on torch tensors (on the current stream by default).
+
+        x: GPU tensor holding the matrix (bf16 or fp32, or int16/uint16/int32
+           bit patterns of the same width), laid out as given at creation.
+        values/ids: optional preallocated outputs (C*k elements each).
+        Returns (values, ids) shaped (C, k).
+        """
+        import torch
+        if not x.is_cuda:
+            raise ValueError("x must be a GPU tensor")
+        need = (self.C - 1) * self.ld + self.V if self.layout == "col" else (self.V - 1) * self.ld + self.C
+        if x.numel() < need or x.element_size() != (2 if self.dtype == "bf16" else 4):
+            raise ValueError("x does not hold the matrix described at creation")
+        if not x.is_contiguous():
+            raise ValueError("x must be contiguous")
+        if values is None:
+            values = torch.empty((self.C, self.k), dtype=x.dtype, device=x.device)
+        if ids is None:
+            ids = torch.empty((self.C, self.k), dtype=torch.int32, device=x.device)
+        if values.numel() < self.C * self.k or ids.numel() < self.C * self.k:
+            raise ValueError("output buffers are too small")
+        s = stream if stream is not None else torch.cuda.current_stream(x.device)
+        self.run_ptr(x.data_ptr(), values.data_ptr(), ids.data_ptr(), s.cuda_stream)
+        return values, ids
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) and self._h.value:
+            rc = load().topk_cols_destroy(self._h)
+            self._h = ctypes.c_void_p()
+            if rc != TOPK_OK:
+                raise TopkError(rc, "topk_cols_destroy")
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def topk_cols(x, V: int, C: int, k: int, dtype: str = "bf16", layout: str = "col", ld=None):
+    """One-shot convenience: create, run, synchronize, destroy."""
+    import torch
+    with TopkCols(V, C, k, dtype, layout, ld) as h:
+        v, i = h.run(x)
+        torch.cuda.current_stream(x.device).synchronize()
+        return v, i

@@ -1,0 +1,139 @@
+/*
+ * topk_cols: column-wise top-k over a speculative drafter's vocabulary logits,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes (ignis docs, page "DFlash2", section "How it works"):
+ * for every column of a V-row logit matrix, select the k largest values and
+ * their row ids, largest first, with ties broken toward the smaller row id.
+ * The result is bit-identical to a plain per-column sort, so draft acceptance
+ * cannot move.  A column is one draft position; the page's drafter proposes 7
+ * per lane over a 248,046-token vocabulary (56 columns at eight lanes).
+ *
+ * The page leaves three points open.  This library reads them as follows.
+ *   - Values compare as real numbers, so -0 equals +0 and a tie between them
+ *     goes to the smaller row.  Subnormals compare exactly; nothing is flushed.
+ *   - NaN of any sign or payload ranks above +Inf, and all NaNs tie with each
+ *     other (the smaller row wins).
+ *   - out_values holds the stored bit pattern of the selected element, so -0
+ *     stays -0 and a NaN keeps its payload.
+ *
+ * Lifecycle: create a handle once per shape, run it any number of times,
+ * destroy it.  All functions return a topk_status; none aborts or throws.
+ */
+#ifndef TOPK_COLS_H
+#define TOPK_COLS_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TOPK_OK = 0,
+    TOPK_ERR_INVALID_ARG = -1,  /* an argument is out of range, NULL or misaligned */
+    TOPK_ERR_UNSUPPORTED = -2,  /* valid, but beyond this build's limits (k > TOPK_MAX_K, V > TOPK_MAX_V) */
+    TOPK_ERR_HIP = -3,          /* a HIP runtime call failed (no device, launch error, ...) */
+    TOPK_ERR_OUT_OF_MEMORY = -4 /* the workspace could not be allocated */
+} topk_status;
+
+typedef enum {
+    TOPK_BF16 = 0, /* bfloat16 stored as 16-bit patterns */
+    TOPK_F32 = 1   /* IEEE binary32 */
+} topk_dtype;
+
+typedef enum {
+    TOPK_COL_CONTIG = 0,     /* element (row r, column c) at x[c*ld + r], ld >= V */
+    TOPK_ROW_INTERLEAVED = 1 /* element (row r, column c) at x[r*ld + c], ld >= C */
+} topk_layout;
+
+/* Largest k accepted. */
+#define TOPK_MAX_K 64
+/* Largest V accepted (row ids must fit in 24 bits). */
+#define TOPK_MAX_V ((int64_t)((1 << 24) - 1))
+
+typedef struct topk_cols *topk_cols_t;
+
+/*
+ * Create a handle for one shape on the current HIP device.
+ *
+ * V: rows (the vocabulary), 1 <= V <= TOPK_MAX_V.
+ * C: columns (draft positions), >= 1.
+ * k: 1 <= k <= V and k <= TOPK_MAX_K.
+ * dtype, layout: see the enums.
+ * ld: leading dimension in elements, ld >= V (column-contiguous) or ld >= C
+ *     (row-interleaved).  Elements in the padding are never read.
+ *
+ * The handle owns a small device workspace (per-block partial results and
+ * per-column counters).  Create allocates it on the current device with
+ * hipMalloc, zeroes it and waits for the zeroing to finish; create is not
+ * meant for the hot loop.
+ *
+ * On any failure *out is set to NULL, and nothing stays allocated.
+ * Returns TOPK_ERR_INVALID_ARG for a bad argument or a NULL out.
+ * Returns TOPK_ERR_UNSUPPORTED when k > TOPK_MAX_K or V > TOPK_MAX_V.
+ * Returns TOPK_ERR_HIP when there is no usable device.
+ * Returns TOPK_ERR_OUT_OF_MEMORY when the allocation fails.
+ */
+int topk_cols_create(topk_cols_t *out, int64_t V, int64_t C, int32_t k, int32_t dtype,
+                     int32_t layout, int64_t ld);
+
+/*
+ * Select the top k of every column.
+ *
+ * logits: device pointer to the matrix described at create.  It must be
+ *         aligned to the element size.
+ * out_values: device, C*k elements of the input dtype, aligned to the element
+ *         size.  out_values[c*k + j] is the j-th largest of column c; j = 0 is
+ *         the largest.
+ * out_ids: device, C*k int32, 4-byte aligned.  out_ids[c*k + j] is the 0-based
+ *         row of out_values[c*k + j].
+ * stream: the HIP stream to enqueue on (0 = the null stream).
+ *
+ * Asynchronous: run only enqueues kernels.  It does not synchronize and does
+ * not allocate.  The outputs are valid once the stream reaches this point.
+ * The caller keeps ownership of all three buffers.  Runs on one handle must be
+ * ordered on a single stream: the workspace serves one run at a time.  Use a
+ * separate handle for each stream that runs concurrently.
+ *
+ * Returns TOPK_ERR_INVALID_ARG for a NULL or misaligned pointer, or a NULL
+ * handle.  Returns TOPK_ERR_HIP when the launch fails.
+ */
+int topk_cols_run(topk_cols_t h, const void *logits, void *out_values, int32_t *out_ids,
+                  hipStream_t stream);
+
+/* Free the handle and its workspace.  NULL is accepted and returns TOPK_OK.
+ * The caller must ensure no run on the handle is still in flight. */
+int topk_cols_destroy(topk_cols_t h);
+
+/* A static, human-readable name for a status code.  Never NULL. */
+const char *topk_cols_status_string(int status);
+
+/*
+ * Like topk_cols_create, but with the vocabulary-axis split fixed to
+ * `segments` workgroups per column (row segments for the interleaved layout)
+ * instead of the automatic choice; 0 means automatic.  For tests and tuning:
+ * the result is the same for every split.  segments * k must not exceed 4096
+ * (TOPK_ERR_UNSUPPORTED otherwise); negative values are TOPK_ERR_INVALID_ARG.
+ */
+int topk_cols_create_with_segments(topk_cols_t *out, int64_t V, int64_t C, int32_t k,
+                                   int32_t dtype, int32_t layout, int64_t ld, int64_t segments);
+
+/*
+ * Introspection for tests and benchmarks.  Writes the launch decomposition
+ * chosen at create.
+ * segments: workgroups per column (vocabulary-axis split) for the
+ *           column-contiguous kernel, or row segments for the interleaved one.
+ * blocks: total workgroups of the main kernel.
+ * workspace_bytes: device bytes owned by the handle.
+ * Any output pointer may be NULL.
+ */
+int topk_cols_query(topk_cols_t h, int64_t *segments, int64_t *blocks, int64_t *workspace_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOPK_COLS_H */

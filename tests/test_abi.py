@@ -1,0 +1,105 @@
+"""The C ABI on a host without a GPU: the library loads, exports every function
+include/topk_cols.h declares, refuses invalid arguments before touching a
+device, and fails cleanly (TOPK_ERR_HIP, NULL handle) when no device exists."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from drafter_vocab_top_amd import topk_cols as T
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", n) for n in os.listdir(os.path.join(ROOT, "include"))
+           if n.endswith(".h")]
+
+
+def declared_functions():
+    names = []
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(topk_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(T.LIBRARY):
+        pytest.fail("libtopk_cols.so is not built (run __graft_entry__.build())")
+    return T.load()
+
+
+def test_header_declares_the_expected_entry_points():
+    assert set(declared_functions()) == set(T.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", T.LIBRARY], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (\w+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings_cover_every_code(lib):
+    for code in (T.TOPK_OK, T.TOPK_ERR_INVALID_ARG, T.TOPK_ERR_UNSUPPORTED, T.TOPK_ERR_HIP,
+                 T.TOPK_ERR_OUT_OF_MEMORY):
+        s = T.status_string(code)
+        assert s and "unknown" not in s
+    assert "unknown" in T.status_string(12345)
+
+
+def _create(lib, *args, segments=None):
+    h = ctypes.c_void_p(0xDEAD)
+    if segments is None:
+        rc = lib.topk_cols_create(ctypes.byref(h), *args)
+    else:
+        rc = lib.topk_cols_create_with_segments(ctypes.byref(h), *args, segments)
+    return rc, h
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((0, 7, 1, 0, 0, 1), T.TOPK_ERR_INVALID_ARG),            # V < 1
+    ((10, 0, 1, 0, 0, 10), T.TOPK_ERR_INVALID_ARG),          # C < 1
+    ((10, 7, 0, 0, 0, 10), T.TOPK_ERR_INVALID_ARG),          # k < 1
+    ((10, 7, 11, 0, 0, 10), T.TOPK_ERR_INVALID_ARG),         # k > V
+    ((10, 7, 1, 2, 0, 10), T.TOPK_ERR_INVALID_ARG),          # unknown dtype
+    ((10, 7, 1, 0, 2, 10), T.TOPK_ERR_INVALID_ARG),          # unknown layout
+    ((10, 7, 1, 0, 0, 9), T.TOPK_ERR_INVALID_ARG),           # ld < V (column-contiguous)
+    ((10, 7, 1, 0, 1, 6), T.TOPK_ERR_INVALID_ARG),           # ld < C (row-interleaved)
+    ((100, 7, 65, 0, 0, 100), T.TOPK_ERR_UNSUPPORTED),       # k > TOPK_MAX_K
+    ((1 << 24, 7, 8, 0, 0, 1 << 24), T.TOPK_ERR_UNSUPPORTED),  # V > TOPK_MAX_V
+])
+def test_invalid_arguments_refused_without_a_device(lib, args, expect):
+    rc, h = _create(lib, *args)
+    assert rc == expect
+    assert h.value is None          # *out is NULL after any failure
+
+
+def test_negative_segments_refused(lib):
+    rc, h = _create(lib, 100, 7, 8, 0, 0, 100, segments=-1)
+    assert rc == T.TOPK_ERR_INVALID_ARG and h.value is None
+    rc, h = _create(lib, 100000, 7, 64, 0, 0, 100000, segments=65)
+    assert rc == T.TOPK_ERR_UNSUPPORTED and h.value is None
+
+
+def test_null_out_pointer_refused(lib):
+    assert lib.topk_cols_create(None, 10, 7, 1, 0, 0, 10) == T.TOPK_ERR_INVALID_ARG
+
+
+def test_null_handle_calls(lib):
+    assert lib.topk_cols_destroy(None) == T.TOPK_OK
+    assert lib.topk_cols_run(None, 16, 16, 16, None) == T.TOPK_ERR_INVALID_ARG
+    assert lib.topk_cols_query(None, None, None, None) == T.TOPK_ERR_INVALID_ARG
+
+
+def test_valid_create_without_a_device_fails_cleanly(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    rc, h = _create(lib, 248046, 7, 8, 0, 0, 248046)
+    assert rc == T.TOPK_ERR_HIP
+    assert h.value is None
