@@ -1,0 +1,369 @@
+#!/usr/bin/env python3
+"""Benchmark: column-wise vocabulary top-k on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one call of the whole path: topk_cols_run on one logit matrix,
+that is one lane-round of a speculative drafter.  The headline workload is a
+248,046 x 7 bf16 matrix with k = 8, column-contiguous: one lane of seven
+drafts, as on the ignis "DFlash2" page, section "How it works".  The inputs
+are already in HBM when timing starts.  They rotate over at least 1 GiB of
+distinct copies, so every round reads cold HBM and not the 256 MB Infinity
+Cache.
+
+The script prints one JSON line on stdout.  Progress goes to stderr.
+  value / ms_per_step  microseconds (milliseconds) per round: K back-to-back
+                       calls between two events on the launch stream, divided
+                       by K.
+  roofline             algorithmic bytes per launch (every element read once
+                       plus the outputs written), divided by the kernel's mean
+                       duration.  The duration comes from an event pair around
+                       each of K calls on the same stream.  Peak is 8 TB/s
+                       HBM3E.  traffic is the HBM bytes per launch measured by
+                       rocprofv3 counters, scaled by a plain copy of known
+                       size (profiles/*_traffic.json).  It is null when the
+                       kernel source changed after the counters were taken.
+  per_config           the same measurements for all five workloads, with the
+                       launch floor of an empty kernel and the warm-cache
+                       figure.
+  cpu_baseline         the CPU oracle timed on this host's cores on whole
+                       rounds of the headline workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, AMD's published peak
+ROTATE_BYTES = 1 << 30          # > 4x the 256 MB Infinity Cache
+HEADLINE = 2                    # 248,046 x 7, k = 8, bf16, column-contiguous
+METRIC = "top-k us/round and HBM GB/s (% peak) at V=248,046, C=7 and C=56"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sources_digest() -> str:
+    from drafter_vocab_top_amd import build as B
+    h = hashlib.sha256()
+    for p in sorted(B.SOURCES + B.HEADERS):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w) -> int:
+    """Every matrix element read once, the k values and ids written once."""
+    return w.V * w.C * w.element_bytes + w.C * w.k * (w.element_bytes + 4)
+
+
+class Rotation:
+    """R device copies of one matrix, each at a 256-byte aligned base."""
+
+    def __init__(self, torch, w, min_bytes=ROTATE_BYTES, copies=None):
+        import numpy as np
+        flat = np.ascontiguousarray(w.x).reshape(-1)
+        view = flat.view(np.int16 if flat.dtype == np.uint16 else np.int32)
+        n = view.size
+        per = (n * view.itemsize + 255) // 256 * 256 // view.itemsize
+        self.R = copies or max(2, -(-min_bytes // (per * view.itemsize)))
+        src = torch.from_numpy(view).to("cuda")
+        self.buf = torch.empty(self.R * per, dtype=src.dtype, device="cuda")
+        for r in range(self.R):
+            self.buf[r * per:r * per + n].copy_(src)
+        self.ptrs = [self.buf[r * per:].data_ptr() for r in range(self.R)]
+        self.first = self.buf[:n]
+        torch.cuda.synchronize()
+
+
+def time_config(torch, T, w, steps, warmup, per_call_steps=None, warm=True):
+    """Amortized and per-call timings of one workload (cold HBM by rotation)."""
+    import numpy as np
+    rot = Rotation(torch, w)
+    h = T.TopkCols(w.V, w.C, w.k, w.dtype, w.layout, w.ld)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    vals = torch.empty((w.C, w.k), dtype=rot.buf.dtype, device="cuda")
+    ids = torch.empty((w.C, w.k), dtype=torch.int32, device="cuda")
+    pv, pi = vals.data_ptr(), ids.data_ptr()
+    run = T.load().topk_cols_run
+    hh = h._h
+    R, ptrs = rot.R, rot.ptrs
+
+    for s in range(warmup):
+        run(hh, ptrs[s % R], pv, pi, sp)
+    torch.cuda.synchronize()
+
+    # amortized: one event pair around `steps` back-to-back calls
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_host = time.perf_counter()
+    e0.record(stream)
+    for s in range(steps):
+        run(hh, ptrs[s % R], pv, pi, sp)
+    e1.record(stream)
+    host_us = (time.perf_counter() - t_host) * 1e6 / steps
+    e1.synchronize()
+    amort_us = e0.elapsed_time(e1) * 1000.0 / steps
+
+    # per call: an event pair around each call, all enqueued back to back
+    n_pc = per_call_steps or steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_pc)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_pc)]
+    for s in range(n_pc):
+        starts[s].record(stream)
+        run(hh, ptrs[s % R], pv, pi, sp)
+        ends[s].record(stream)
+    torch.cuda.synchronize()
+    per_call = sorted(starts[s].elapsed_time(ends[s]) * 1000.0 for s in range(n_pc))
+
+    res = {
+        "us_per_round": amort_us,
+        "host_enqueue_us_per_call": host_us,
+        "per_call_mean_us": statistics.fmean(per_call),
+        "per_call_median_us": per_call[len(per_call) // 2],
+        "per_call_p10_us": per_call[len(per_call) // 10],
+        "per_call_p90_us": per_call[(9 * len(per_call)) // 10],
+        "rotation_copies": R,
+        "decomposition": h.query(),
+    }
+    if warm:
+        p0 = ptrs[0]
+        for s in range(warmup):
+            run(hh, p0, pv, pi, sp)
+        e0.record(stream)
+        for s in range(steps):
+            run(hh, p0, pv, pi, sp)
+        e1.record(stream)
+        e1.synchronize()
+        res["warm_us_per_round"] = e0.elapsed_time(e1) * 1000.0 / steps
+    # the timed outputs must be the right answer: compare the last call's
+    # result with a fresh run on the same input (cheap self-check)
+    run(hh, ptrs[(n_pc - 1) % R], pv, pi, sp)
+    torch.cuda.synchronize()
+    res["_last"] = (vals.cpu().numpy(), ids.cpu().numpy())
+    h.close()
+    del rot
+    torch.cuda.empty_cache()
+    return res
+
+
+def launch_floor(torch, steps):
+    """Back-to-back empty-kernel launches (torch's sleep kernel with 0 cycles),
+    captured in a graph so host overhead does not count."""
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(0)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(200):
+                torch.cuda._sleep(0)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(1, steps // 200)
+    with torch.cuda.stream(stream):
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+    e1.synchronize()
+    return e0.elapsed_time(e1) * 1000.0 / (reps * 200)
+
+
+def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0):
+    """The oracle, as it stands, on whole rounds of workload w on host cores."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    threads = max(1, min(w.C, cores))
+    odt = oracle.BF16 if w.dtype == "bf16" else oracle.F32
+    oly = oracle.COL_CONTIG if w.layout == "col" else oracle.ROW_INTERLEAVED
+    oracle.topk_cols(w.x, w.V, w.C, w.k, odt, oly, w.ld, nthreads=threads)  # load + warm
+    times = []
+    t_end = time.perf_counter() + min_seconds
+    t_cap = time.perf_counter() + max_seconds
+    while (time.perf_counter() < t_end or len(times) < 3) and time.perf_counter() < t_cap:
+        t0 = time.perf_counter()
+        res = oracle.topk_cols(w.x, w.V, w.C, w.k, odt, oly, w.ld, nthreads=threads)
+        times.append(time.perf_counter() - t0)
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {
+        "value": statistics.median(times) * 1e6,
+        "unit": "us/round",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{len(times)} whole rounds of {w.name} ({w.C} columns x {w.V} rows), "
+                  f"median, {sum(times):.1f} s of CPU work, threads over columns",
+        "host_cores_available": cores,
+        "cpu_model": cpu,
+    }, res
+
+
+def device_info(torch):
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "gcn_arch": getattr(p, "gcnArchName", ""),
+            "cu_count": p.multi_processor_count, "memory_gb": round(p.total_memory / 2**30, 1),
+            "torch": torch.__version__, "hip": torch.version.hip, "host": platform.node()}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm"] = f.read().strip()
+    except OSError:
+        pass
+    return info
+
+
+def traffic_record(digest, config_n):
+    path = os.path.join(ROOT, "profiles", f"topk_col_cfg{config_n}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sources_digest") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--configs", default="1,2,3,4,5",
+                    help="workloads measured for per_config (the headline is always measured)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="profiling run: headline workload only, few steps, plus a copy of known size")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this path has no multi-GPU mode "
+              "(columns are independent; see DESIGN.md for how it would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from drafter_vocab_top_amd import topk_cols as T
+    from drafter_vocab_top_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    T.load()
+    digest = kernel_sources_digest()
+
+    if args.profile:
+        w = W.config(HEADLINE)
+        res = time_config(torch, T, w, args.steps, args.warmup, warm=False)
+        # a plain copy of known size, for scaling the traffic counters
+        src = torch.empty(64 << 20, dtype=torch.int32, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"profile run: {w.name} {res['us_per_round']:.2f} us/round; copy of {src.numel() * 4} bytes x5")
+        return
+
+    log(f"device: {device_info(torch)}")
+    per_config = {}
+    floor_us = launch_floor(torch, 2000)
+    log(f"launch floor (empty kernel, graph): {floor_us:.3f} us")
+    wanted = sorted(set(int(c) for c in args.configs.split(",") if c) | {HEADLINE})
+    headline = None
+    for n in wanted:
+        shape = W.config_shape(n)
+        w = W.config(n)
+        steps = args.steps if n == HEADLINE else (200 if n == 5 else 1000)
+        warmup = args.warmup if n == HEADLINE else 50
+        log(f"timing {w.name}: {steps} steps, warmup {warmup}")
+        try:
+            r = time_config(torch, T, w, steps, warmup)
+        except T.TopkError as e:
+            per_config[f"cfg{n}"] = {"workload": w.name, "error": str(e)}
+            log(f"  {e}")
+            continue
+        import oracle
+        odt = oracle.BF16 if w.dtype == "bf16" else oracle.F32
+        oly = oracle.COL_CONTIG if w.layout == "col" else oracle.ROW_INTERLEAVED
+        ov, oi = oracle.topk_cols(w.x, w.V, w.C, w.k, odt, oly, w.ld, nthreads=8)
+        gv, gi = r.pop("_last")
+        st = np.uint16 if w.dtype == "bf16" else np.uint32
+        exact = bool(np.array_equal(gi, oi) and np.array_equal(gv.view(st), ov.view(st)))
+        b = algorithmic_bytes(w)
+        floor = max(b / (PEAK_HBM_GBPS * 1e3), floor_us)
+        r.update({
+            "workload": w.name, "V": w.V, "C": w.C, "k": w.k, "dtype": w.dtype, "layout": w.layout,
+            "algorithmic_bytes": b,
+            "gbps": b / (r["us_per_round"] * 1e3),
+            "frac_of_peak": b / (r["us_per_round"] * 1e3) / PEAK_HBM_GBPS,
+            "kernel_gbps": b / (r["per_call_mean_us"] * 1e3),
+            "hbm_floor_us": b / (PEAK_HBM_GBPS * 1e3),
+            "floor_us": floor,
+            "ratio_to_floor": r["us_per_round"] / floor,
+            "bit_exact_vs_oracle": exact,
+        })
+        per_config[f"cfg{n}"] = r
+        log(f"  {r['us_per_round']:.2f} us/round (per call {r['per_call_median_us']:.2f} us, "
+            f"warm {r.get('warm_us_per_round', float('nan')):.2f} us, host {r['host_enqueue_us_per_call']:.2f} us), "
+            f"{r['gbps']:.0f} GB/s = {100 * r['frac_of_peak']:.1f}% of peak, exact={exact}")
+        if n == HEADLINE:
+            headline = (w, r)
+
+    w, r = headline
+    traffic = traffic_record(digest, HEADLINE)
+    b = algorithmic_bytes(w)
+    achieved = b / (r["per_call_mean_us"] * 1e3)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle (cpu_baseline) ...")
+        cpu, _ = cpu_baseline(w)
+        log(f"  oracle: {cpu['value']:.0f} us/round on {cpu['cores']} threads")
+    out = {
+        "metric": METRIC,
+        "value": round(r["us_per_round"], 3),
+        "unit": "us/round",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["us_per_round"] / 1000.0,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u64",
+        "data": "synthetic (seeded, BASELINE.json configs; inputs resident in HBM, rotated over >=1 GiB)",
+        "config": {"workload": w.name, "V": w.V, "C": w.C, "k": w.k, "input_dtype": w.dtype,
+                   "layout": w.layout, "ld": w.ld, "segments": r["decomposition"]["segments"],
+                   "blocks": r["decomposition"]["blocks"]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
+                     "algorithmic_bytes": b, "kernel_mean_us": r["per_call_mean_us"]},
+        "cpu_baseline": cpu,
+        "launch_floor_us": floor_us,
+        "per_config": per_config,
+        "kernel_sources_digest": digest,
+        "device": device_info(torch),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

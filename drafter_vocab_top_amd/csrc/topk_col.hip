@@ -2,42 +2,48 @@
 //
 // The ignis "DFlash2" page ("How it works") explains why the replacement
 // top-k was fast: it split each column's vocabulary rows across workgroups
-// and kept k in registers.  This kernel keeps the split and does the rest
-// differently.  Each column's V rows are cut into S segments, and one 256-lane
-// workgroup scans each segment, so C*S workgroups fill the 256 CUs even at
-// C = 7.  A workgroup reduces its segment to a sorted top-k; the last
-// workgroup of each column to finish merges the S partial lists and writes
-// the answer.
+// and kept k in registers.  This kernel keeps that split.  Each column's V
+// rows are cut into S segments, and one 256-lane workgroup scans each
+// segment, so C*S workgroups fill the 256 CUs even at C = 7.  The rest is
+// built for wave64 CDNA and for latency: at these sizes one round trip to
+// memory costs about a microsecond and a lone wave about 3 ns per
+// instruction, so the design minimises both on the critical path.
 //
-// A scan pass, per workgroup:
-//  1. Every lane loads NV 16-byte vectors with coalesced loads.  Vectors are
-//     aligned to 16 bytes; the unaligned head and tail rows of the column
-//     (fewer than one vector each) go to a few lanes of the first and last
-//     segment as single "edge" elements.
-//  2. Each lane takes the exact maximum order of its elements with packed
-//     16-bit (bf16) or 32-bit integer max/min on the raw bit patterns, never
-//     on converted floats.  The signed-integer maximum of raw patterns is the
+// One scan pass:
+//  1. Each lane loads NV 16-byte vectors (coalesced: 64 lanes x 16 bytes),
+//     NV in {2, 4, 8} picked so that a segment takes one pass when it can.
+//     Vectors are aligned to 16 bytes.  The column's unaligned head and tail
+//     rows, fewer than one vector each, go to lanes of wave 0 in the first
+//     and last segment as single "edge" elements.
+//  2. Each lane takes the exact maximum order of its elements.  It uses
+//     packed 16-bit (bf16) or 32-bit integer max/min on the raw bit patterns,
+//     never converted floats.  The signed maximum of raw patterns is the
 //     largest non-negative value; when a lane holds only negative patterns,
 //     the signed minimum is its largest value.
-//  3. Each wave finds the k-th largest lane maximum with a ballot bit-search,
-//     and the workgroup takes the largest of those.  The result T is a lower
-//     bound on the workgroup's k-th largest value.  Any element below T
-//     cannot be in the top-k.
-//  4. Elements whose value is at least T (usually about k to 2k of them) are
-//     appended as 64-bit keys to an LDS buffer.  They are found with a
-//     per-vector prefilter and an integer interval test on the raw pattern.
-//  5. A rank count over the buffer picks the exact top-k.  It is carried as
-//     a running threshold into the next pass, if the segment needs several.
-// Negative NaNs, or more candidates than the buffer holds (massive ties),
-// switch that pass to an exact block-wide bit search over the keys.
+//  3. Each wave, on its own, finds T, the k-th largest of its lanes' maxima,
+//     with a ballot bit-search.  k lanes hold an element at or above T, so
+//     no element below T can be in the wave's top-k, let alone the segment's.
+//  4. The wave's elements at or above T (usually about k of them) are found
+//     with a per-vector prefilter and an integer interval test on the raw
+//     pattern.  Ballot/mbcnt compaction collects them as 64-bit keys in the
+//     wave's LDS area.  The wave then copies them after the carried best
+//     keys in the workgroup area (one LDS atomic per wave).
+//  5. After one workgroup barrier, a rank count over that area gives the
+//     segment's exact top-k.  A segment that needs several passes carries it
+//     into the next pass as a running threshold.
+// Negative NaNs, more candidates than a wave's area holds, or more than the
+// workgroup's (massive ties), send that pass to an exact path.  There, each
+// wave finds its own top-k by a wave-wide bit search over the keys.
 //
 // Cross-workgroup merge without cache-flushing fences.  Each workgroup
-// publishes its k keys with device-scope atomic stores, which write through
-// the XCD's L2.  It then increments the column's ticket.  Every key carries
-// the run's tag, so the workgroup that draws the last ticket reads the other
-// lists with device-scope loads and re-reads any slot whose tag is stale
-// until its store lands.  That workgroup merges the lists, writes the output
-// and resets the ticket for the next run.
+// publishes its sorted k keys with device-scope atomic stores, which write
+// through the XCD's L2.  It then takes the column's ticket, a device-scope
+// atomic on a 128-byte line of its own.  Every key carries the run's tag, so
+// the workgroup that draws the last ticket reads the S lists with
+// device-scope loads.  It re-reads any slot whose tag is stale until that
+// store lands.  All four of its waves then select from the S*k keys: per-wave
+// thresholds, one barrier, one rank count.  It writes the output and resets
+// the ticket for the next run.
 #include "topk_device.hpp"
 #include "topk_internal.hpp"
 
@@ -45,24 +51,29 @@ namespace topk {
 
 namespace {
 
+static_assert(kWaves == kColWavesPerBlock, "host and kernel disagree on waves per workgroup");
+
+constexpr int kWaveCap = 192;                // candidate slots per wave
+constexpr int kBlockCap = 512;               // carried best + candidates per workgroup
+constexpr int kMergeKeysPerThread = 16;      // S*k <= 4096 published keys, 16 per thread
+constexpr int kSpinLimit = 1 << 16;          // about 0.1 s: a store that has not landed by then never will
+
 struct ColShared {
-    uint64_t cand[kCandCap];   // candidate keys
-    uint64_t best[kMaxK];      // current top-k, sorted
+    alignas(16) uint64_t cand[kBlockCap];          // [0, nbest) carried best, then candidates
+    alignas(16) uint64_t best[kMaxK];              // rank-selection output, sorted
+    alignas(16) uint64_t wbuf[kWaves][kWaveCap];   // each wave's candidates
+    alignas(16) uint64_t wtmp[kWaves][kMaxK];      // each wave's exact-path result
     uint32_t wave_thr[kWaves];
-    uint32_t red[3];           // block_sum rotation slots
-    uint32_t flags[2];         // per-pass "exact path needed" flags, alternating
-    uint32_t cnt;
+    uint32_t ncand;
+    uint32_t overflow;
     uint32_t is_last;
 };
-
-constexpr int kSpinLimit = 1 << 16;  // about 0.1 s: a store that has not landed by then never will
-constexpr int kMergeKeysPerThread = kMaxMergeKeys / kBlock;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ u32x4 load_vec(const u32x4* p) { return __builtin_nontemporal_load(p); }
 
-// Raw pattern of element e (0 <= e < kPerVec) of a loaded vector.
+// Raw pattern of element e (0 <= e < kPerVec, known at compile time).
 template <class DT>
 __device__ __forceinline__ uint32_t vec_elem(const u32x4& v, int e) {
     const uint32_t w = e < DT::kPerVec / 4 ? v.x
@@ -72,13 +83,24 @@ __device__ __forceinline__ uint32_t vec_elem(const u32x4& v, int e) {
     else return w;
 }
 
+// Raw pattern of element e, e known only at run time.
+template <class DT>
+__device__ __forceinline__ uint32_t vec_elem_dyn(const u32x4& v, uint32_t e) {
+    const uint32_t q = DT::kPerVec == 8 ? e >> 1 : e;
+    const uint32_t wx = v.x, wy = v.y, wz = v.z, ww = v.w;
+    const uint32_t w = q == 0 ? wx : q == 1 ? wy : q == 2 ? wz : ww;
+    if constexpr (DT::kPerVec == 8) return (w >> ((e & 1u) * 16u)) & 0xFFFFu;
+    else return w;
+}
+
 __device__ __forceinline__ s16x2 as_s16x2(uint32_t w) { return __builtin_bit_cast(s16x2, w); }
 __device__ __forceinline__ u16x2 as_u16x2(uint32_t w) { return __builtin_bit_cast(u16x2, w); }
 
-// Lane statistics of one pass (see step 2 above).
+// Lane statistics of one pass (step 2).
 //   vmax[i]: raw signed maximum of vector i (bf16: two 16-bit halves packed)
 //   rep:     exact maximum order over the lane's elements, unless the lane
 //            holds a negative NaN (then neg_nan is set and rep is unused)
+// Invalid vector slots hold -Inf patterns, which never raise a maximum.
 template <class DT, int NV>
 __device__ __forceinline__ void lane_stats(const u32x4 (&d)[NV], uint32_t (&vmax)[NV],
                                            uint32_t& rep, bool& neg_nan) {
@@ -103,21 +125,22 @@ __device__ __forceinline__ void lane_stats(const u32x4 (&d)[NV], uint32_t (&vmax
             smin = __builtin_elementwise_min(smin, mn);
             umax = __builtin_elementwise_max(umax, ux);
         }
-        const int M = max((int)smax.x, (int)smax.y);
-        const int m = min((int)smin.x, (int)smin.y);
+        const int M = max_i32((int)smax.x, (int)smax.y);
+        const int m = min_i32((int)smin.x, (int)smin.y);
         rep = M >= 0 ? order_bf16((uint32_t)M) : order_bf16((uint32_t)m & 0xFFFFu);
-        neg_nan = max((uint32_t)umax.x, (uint32_t)umax.y) > 0xFF80u;
+        neg_nan = max_u32((uint32_t)umax.x, (uint32_t)umax.y) > 0xFF80u;
     } else {
         int smax = INT32_MIN, smin = INT32_MAX;
         uint32_t umax = 0;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const int a = (int)d[i].x, b = (int)d[i].y, c = (int)d[i].z, e = (int)d[i].w;
-            const int mx = max(max(a, b), max(c, e));
+            const uint32_t wx = d[i].x, wy = d[i].y, wz = d[i].z, ww = d[i].w;
+            const int a = (int)wx, b = (int)wy, c = (int)wz, e = (int)ww;
+            const int mx = max_i32(max_i32(a, b), max_i32(c, e));
             vmax[i] = (uint32_t)mx;
-            smax = max(smax, mx);
-            smin = min(smin, min(min(a, b), min(c, e)));
-            umax = max(umax, max(max(d[i].x, d[i].y), max(d[i].z, d[i].w)));
+            smax = max_i32(smax, mx);
+            smin = min_i32(smin, min_i32(min_i32(a, b), min_i32(c, e)));
+            umax = max_u32(umax, max_u32(max_u32(wx, wy), max_u32(wz, ww)));
         }
         rep = smax >= 0 ? order_f32((uint32_t)smax) : order_f32((uint32_t)smin);
         neg_nan = umax > 0xFF800000u;
@@ -129,51 +152,133 @@ template <class DT>
 __device__ __forceinline__ int vec_max_signed(uint32_t vm) {
     if constexpr (DT::kPerVec == 8) {
         const s16x2 h = as_s16x2(vm);
-        return max((int)h.x, (int)h.y);
+        return max_i32((int)h.x, (int)h.y);
     } else {
         return (int)vm;
     }
 }
 
-__device__ __forceinline__ void append(ColShared& sh, uint64_t key) {
-    const uint32_t idx = atomicAdd(&sh.cnt, 1u);
-    if (idx < (uint32_t)kCandCap) sh.cand[idx] = key;
-}
-
-// Exact top-k of the keys the threads hold: a block-wide bit search for the
-// k-th largest key, then a rank count of the (at most k) keys at or above it.
-// visit(f) calls f(key) for every key the calling thread holds.  Writes
-// sh.best[0..n) sorted and returns n = min(k, number of keys).  Keys must be
-// distinct, apart from identical sentinels that never reach the top k.
-template <int OrderBits, class Visit>
-__device__ uint32_t exact_topk(ColShared& sh, const Visit& visit, uint32_t k, uint32_t& phase) {
-    uint32_t local = 0;
-    visit([&](uint64_t) { ++local; });
-    const uint32_t total = block_sum(local, sh.red, phase);
-    uint64_t thr = 0;
-    if (total > k) {
-        for (int b = 32 + OrderBits - 1; b >= 8; --b) {
-            const uint64_t cand = thr | (1ull << b);
-            uint32_t n = 0;
-            visit([&](uint64_t key) { n += key >= cand ? 1u : 0u; });
-            if (block_sum(n, sh.red, phase) >= k) thr = cand;
-        }
+// Copy a wave's m keys (src, LDS) into the workgroup area behind what other
+// waves have added (one LDS atomic for the wave's base).  Sets sh.overflow if
+// they do not fit.
+__device__ __forceinline__ void wave_to_block(ColShared& sh, const uint64_t* src, uint32_t m) {
+    const uint32_t lane = threadIdx.x & 63u;
+    uint32_t base = 0;
+    if (lane == 0 && m != 0) {
+        base = atomicAdd(&sh.ncand, m);
+        if (base + m > (uint32_t)kBlockCap) sh.overflow = 1u;
     }
-    if (threadIdx.x == 0) sh.cnt = 0;
-    __syncthreads();
-    visit([&](uint64_t key) {
-        if (key >= thr) append(sh, key);
-    });
-    __syncthreads();
-    const uint32_t n = min(sh.cnt, (uint32_t)kCandCap);
-    rank_select(sh.cand, n, k, sh.best);
-    __syncthreads();
-    return min(n, k);
+    base = __builtin_amdgcn_readfirstlane(base);
+    for (uint32_t t = lane; t < m; t += 64u)
+        if (base + t < (uint32_t)kBlockCap) sh.cand[base + t] = src[t];
 }
 
-// Device-scope load of a published key, re-read until it carries this run's tag.
+// The exact path of one scan pass for one wave: its own top-k (at most k
+// keys, sorted, in out) over the pass's elements and its edge element.  Rare,
+// so it is kept out of line and re-reads the pass's vectors at every step of
+// its search instead of holding 2*NV*EPV key registers across it.
+template <class DT, int NV>
+__device__ __noinline__ uint32_t exact_scan_wave(uint64_t* wb, uint64_t* out, const u32x4* vec,
+                                                 uint32_t v0, uint32_t ve, uint32_t head, uint64_t ex,
+                                                 uint32_t k, uint32_t tag) {
+    constexpr int EPV = DT::kPerVec;
+    auto visit = [&](auto&& f) {
+#pragma unroll 1
+        for (int i = 0; i < NV; ++i) {
+            const uint32_t vi = v0 + (uint32_t)i * kBlock;
+            const bool valid = vi < ve;
+            const u32x4 v = valid ? vec[vi] : u32x4{0u, 0u, 0u, 0u};
+            const uint32_t row0 = head + vi * EPV;
+#pragma unroll
+            for (int e = 0; e < EPV; ++e)
+                f(make_key(DT::order(vec_elem<DT>(v, e)), row0 + e, tag), valid);
+        }
+        f(ex, ex != 0);
+    };
+    return wave_exact_topk<DT::kOrderBits>(wb, kWaveCap, out, visit, k);
+}
+
+// Device-scope load of a published key (bypasses the non-coherent L2).
 __device__ __forceinline__ uint64_t load_published(const uint64_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Selection by the last workgroup of a column: the top k of the S*k
+// published keys, into sh.best.
+template <class DT>
+__device__ __forceinline__ void merge_lists(const ColArgs& a, ColShared& sh, const uint64_t* parts) {
+    constexpr int OB = DT::kOrderBits;
+    const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
+    const uint32_t k = (uint32_t)a.k, tag = a.tag;
+    const uint32_t M = (uint32_t)a.S * k;
+    // slots j < J hold keys (J = M / 256 rounded up; the later slots are skipped
+    // by a workgroup-uniform test)
+    const uint32_t J = (M + kBlock - 1) / kBlock;
+    uint64_t keys[kMergeKeysPerThread];
+#pragma unroll
+    for (int j = 0; j < kMergeKeysPerThread; ++j) {
+        const uint32_t idx = tid + (uint32_t)j * kBlock;
+        keys[j] = 0;
+        if ((uint32_t)j < J && idx < M) keys[j] = load_published(parts + idx);
+    }
+#pragma unroll
+    for (int j = 0; j < kMergeKeysPerThread; ++j) {
+        const uint32_t idx = tid + (uint32_t)j * kBlock;
+        if ((uint32_t)j < J && idx < M) {
+            for (int spin = 0; key_tag(keys[j]) != tag && spin < kSpinLimit; ++spin) {
+                __builtin_amdgcn_s_sleep(1);
+                keys[j] = load_published(parts + idx);
+            }
+        }
+    }
+    uint64_t rep = 0;
+#pragma unroll
+    for (int j = 0; j < kMergeKeysPerThread; ++j)
+        if ((uint32_t)j < J) rep = max_u64(rep, keys[j]);
+    const uint32_t wt = wave_kth_largest<OB>(key_order(rep), k);
+    if (lane == 0) sh.wave_thr[wave] = wt;
+    if (tid == 0) {
+        sh.ncand = 0;
+        sh.overflow = 0;
+    }
+    __syncthreads();
+    uint32_t T = sh.wave_thr[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) T = max_u32(T, sh.wave_thr[w]);
+
+    // sentinel keys (order 0, from segments with fewer than k rows) never qualify
+    auto visit = [&](auto&& f) {
+#pragma unroll
+        for (int j = 0; j < kMergeKeysPerThread; ++j)
+            if ((uint32_t)j < J) f(keys[j], key_order(keys[j]) != 0);
+    };
+    uint64_t* wb = sh.wbuf[wave];
+    uint32_t cnt = 0;
+    visit([&](uint64_t key, bool valid) {
+        cnt = wave_append(wb, cnt, kWaveCap, valid && key_order(key) >= T, key);
+    });
+    if (cnt > (uint32_t)kWaveCap) {
+        cnt = wave_exact_topk<OB>(wb, kWaveCap, sh.wtmp[wave], visit, k);
+        wave_to_block(sh, sh.wtmp[wave], cnt);
+    } else {
+        wave_to_block(sh, wb, cnt);
+    }
+    __syncthreads();
+    uint32_t n = sh.ncand;
+    if (sh.overflow) {
+        __syncthreads();
+        if (tid == 0) {
+            sh.ncand = 0;
+            sh.overflow = 0;
+        }
+        __syncthreads();
+        const uint32_t m = wave_exact_topk<OB>(wb, kWaveCap, sh.wtmp[wave], visit, k);
+        wave_to_block(sh, sh.wtmp[wave], m);
+        __syncthreads();
+        n = sh.ncand;
+    }
+    rank_select(sh.cand, n, k, sh.best, tid, kBlock);
+    __syncthreads();
 }
 
 template <class DT, int NV>
@@ -183,224 +288,170 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
     constexpr int OB = DT::kOrderBits;
     __shared__ ColShared sh;
 
-    const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
+    const uint32_t tid = threadIdx.x, wave = tid >> 6;
     const uint32_t k = (uint32_t)a.k;
     const uint32_t tag = a.tag;
-    const int64_t c = blockIdx.x / a.S;
-    const int64_t s = blockIdx.x % a.S;
-    const int64_t V = a.V;
-    const storage* col = static_cast<const storage*>(a.x) + c * a.ld;
+    // Rows and vector indices fit in 32 bits (V < 2^24); only the column
+    // offset c * ld needs 64.
+    const uint32_t S = (uint32_t)a.S;
+    const uint32_t c = blockIdx.x / S;
+    const uint32_t s = blockIdx.x - c * S;
+    const uint32_t V = (uint32_t)a.V;
+    const storage* col = static_cast<const storage*>(a.x) + (int64_t)c * a.ld;
 
     // Split the column into an unaligned head, 16-byte vectors and a tail.
-    int64_t head = (int64_t)(((16u - ((uint32_t)(uintptr_t)col & 15u)) & 15u) / sizeof(storage));
+    uint32_t head = ((16u - ((uint32_t)(uintptr_t)col & 15u)) & 15u) / (uint32_t)sizeof(storage);
     if (head > V) head = V;
-    const int64_t nvec = (V - head) / EPV;
-    const int64_t tail0 = head + nvec * EPV;
-    const int64_t vb = nvec * s / a.S, ve = nvec * (s + 1) / a.S;
+    const uint32_t nvec = (V - head) / EPV;
+    const uint32_t tail0 = head + nvec * EPV;
+    const uint32_t vb = nvec * s / S, ve = nvec * (s + 1) / S;
     const u32x4* vec = reinterpret_cast<const u32x4*>(col + head);
 
-    uint64_t edge = 0;  // this lane's edge element, or 0
+    uint64_t edge = 0;  // this lane's edge element (wave 0 only), or 0
     {
-        int64_t row = -1;
-        if (s == 0 && (int64_t)tid < head) row = tid;
-        if (s == a.S - 1 && tid >= 32 && (int64_t)(tid - 32) < V - tail0) row = tail0 + (tid - 32);
-        if (row >= 0) edge = make_key(DT::order(col[row]), (uint32_t)row, tag);
+        uint32_t row = 0xFFFFFFFFu;
+        if (s == 0 && tid < head) row = tid;
+        if (s == S - 1 && tid >= 32 && tid - 32 < V - tail0) row = tail0 + (tid - 32);
+        if (row != 0xFFFFFFFFu) edge = make_key(DT::order(col[row]), row, tag);
     }
-
     if (tid == 0) {
-        sh.red[0] = sh.red[1] = sh.red[2] = 0;
-        sh.flags[0] = sh.flags[1] = 0;
+        sh.ncand = 0;
+        sh.overflow = 0;
     }
     __syncthreads();
-    uint32_t phase = 0;
-    uint32_t nbest = 0;   // keys carried in sh.cand[0..nbest) from earlier passes
-    uint64_t t_run = 0;   // carried k-th best key (valid when nbest == k)
-    const int64_t per_pass = (int64_t)kBlock * NV;
-    const int64_t span = ve - vb;
-    const int64_t npass = span > 0 ? (span + per_pass - 1) / per_pass : 1;
 
-    for (int64_t p = 0; p < npass; ++p) {
-        const int64_t v0 = vb + p * per_pass + tid;
+    uint64_t* wb = sh.wbuf[wave];
+    uint32_t nbest = 0;  // the segment's best so far, in sh.cand[0..nbest) at the start of a pass
+    uint64_t t_run = 0;  // the k-th best key once nbest == k
+    const uint32_t per_pass = (uint32_t)kBlock * NV;
+    const uint32_t npass = ve > vb ? (ve - vb + per_pass - 1) / per_pass : 1u;
+
+    for (uint32_t p = 0; p < npass; ++p) {
+        const uint32_t v0 = vb + p * per_pass + tid;
         u32x4 d[NV];
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const int64_t vi = v0 + (int64_t)i * kBlock;
+            const uint32_t vi = v0 + (uint32_t)i * kBlock;
             d[i] = vi < ve ? load_vec(vec + vi)
                            : u32x4{DT::kFillDword, DT::kFillDword, DT::kFillDword, DT::kFillDword};
         }
-        const int nvalid = ve > v0 ? (int)min((int64_t)NV, (ve - v0 + kBlock - 1) / kBlock) : 0;
+        // vector slots of this lane that hold data
+        const int nvalid = ve > v0 ? (int)min_u32((uint32_t)NV, (ve - v0 + kBlock - 1) / kBlock) : 0;
         const uint64_t ex = p == 0 ? edge : 0;
-        const uint32_t fl = (uint32_t)(p & 1);
 
         uint32_t vmax[NV];
         uint32_t rep;
         bool neg_nan;
         lane_stats<DT, NV>(d, vmax, rep, neg_nan);
-        if (ex) rep = max(rep, key_order(ex));
-        const uint32_t wt = wave_kth_largest<OB>(rep, k);
-        const bool any_nan = __ballot(neg_nan) != 0ull;
-        if (lane == 0) {
-            sh.wave_thr[wave] = wt;
-            if (any_nan) atomicOr(&sh.flags[fl], 1u);
-        }
-        if (tid == 0) {
-            sh.cnt = nbest;
-            sh.flags[fl ^ 1u] = 0;
-        }
-        __syncthreads();
+        if (ex) rep = max_u32(rep, key_order(ex));
+        uint32_t T = wave_kth_largest<OB>(rep, k);
+        if (nbest == k) T = max_u32(T, key_order(t_run));
+        const uint64_t tc = max_u64((uint64_t)T << 32, nbest == k ? t_run + 1 : (uint64_t)0);
 
-        uint32_t T = sh.wave_thr[0];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) T = max(T, sh.wave_thr[w]);
-        if (nbest == k) T = max(T, key_order(t_run));
-        const uint64_t tc = max((uint64_t)T << 32, nbest == k ? t_run + 1 : 0ull);
-        const bool exact = sh.flags[fl] != 0;
+        bool exact = __any(neg_nan);
+        uint32_t cnt = 0;
         if (!exact) {
             RawFilter<DT> f;
             f.set(T);
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
-                if (i < nvalid && (!f.positive || vec_max_signed<DT>(vmax[i]) >= (int)f.lo)) {
-                    const int64_t row0 = head + (v0 + (int64_t)i * kBlock) * EPV;
+                const bool pv = i < nvalid && (!f.positive || vec_max_signed<DT>(vmax[i]) >= (int)f.lo);
+                if (__any(pv)) {
+                    // bit e set: element e is at or above the value threshold
+                    uint32_t m = 0;
+                    if (pv) {
 #pragma unroll
-                    for (int e = 0; e < EPV; ++e) {
-                        const uint32_t raw = vec_elem<DT>(d[i], e);
-                        if (f.pass(raw)) {
-                            const uint64_t key = make_key(DT::order(raw), (uint32_t)(row0 + e), tag);
-                            if (key >= tc) append(sh, key);
-                        }
+                        for (int e = 0; e < EPV; ++e) m |= f.pass(vec_elem<DT>(d[i], e)) ? (1u << e) : 0u;
+                    }
+                    const uint32_t row0 = head + (v0 + (uint32_t)i * kBlock) * EPV;
+                    while (__any(m != 0)) {
+                        const uint32_t e = m != 0 ? (uint32_t)__builtin_ctz(m) : 0u;
+                        const uint64_t key = make_key(DT::order(vec_elem_dyn<DT>(d[i], e)), row0 + e, tag);
+                        cnt = wave_append(wb, cnt, kWaveCap, m != 0 && key >= tc, key);
+                        m &= m - 1u;
                     }
                 }
             }
-            if (ex != 0 && ex >= tc) append(sh, ex);
+            if (wave == 0) cnt = wave_append(wb, cnt, kWaveCap, ex != 0 && ex >= tc, ex);
+            exact = cnt > (uint32_t)kWaveCap;
+        }
+        if (exact) {
+            cnt = exact_scan_wave<DT, NV>(wb, sh.wtmp[wave], vec, v0, ve, head, ex, k, tag);
+            wave_to_block(sh, sh.wtmp[wave], cnt);
+        } else {
+            wave_to_block(sh, wb, cnt);
         }
         __syncthreads();
-
-        const uint32_t cnt = sh.cnt;
-        uint32_t nb;
-        if (exact || cnt > (uint32_t)kCandCap) {
-            const uint64_t carried = tid < nbest ? sh.cand[tid] : 0ull;
-            auto visit = [&](auto&& f) {
-#pragma unroll
-                for (int i = 0; i < NV; ++i) {
-                    if (i < nvalid) {
-                        const int64_t row0 = head + (v0 + (int64_t)i * kBlock) * EPV;
-#pragma unroll
-                        for (int e = 0; e < EPV; ++e)
-                            f(make_key(DT::order(vec_elem<DT>(d[i], e)), (uint32_t)(row0 + e), tag));
-                    }
-                }
-                if (ex) f(ex);
-                if (carried) f(carried);
-            };
-            nb = exact_topk<OB>(sh, visit, k, phase);
-        } else {
-            rank_select(sh.cand, cnt, k, sh.best);
+        uint32_t n = sh.ncand;
+        if (sh.overflow) {
+            // More candidates than the workgroup area holds (massive ties):
+            // every wave reduces its share exactly, then the workgroup selects.
             __syncthreads();
-            nb = min(cnt, k);
+            if (tid == 0) {
+                sh.ncand = nbest;  // the carried best in cand[0..nbest) is intact
+                sh.overflow = 0;
+            }
+            __syncthreads();
+            const uint32_t m = exact_scan_wave<DT, NV>(wb, sh.wtmp[wave], vec, v0, ve, head, ex, k, tag);
+            wave_to_block(sh, sh.wtmp[wave], m);
+            __syncthreads();
+            n = sh.ncand;
         }
-        if (p + 1 < npass && tid < nb) sh.cand[tid] = sh.best[tid];
-        nbest = nb;
-        if (nb == k) t_run = sh.best[k - 1];
+        rank_select(sh.cand, n, k, sh.best, tid, kBlock);
+        __syncthreads();
+        nbest = min_u32(n, k);
+        if (nbest == k) t_run = sh.best[k - 1];
+        if (p + 1 < npass) {
+            if (tid < nbest) sh.cand[tid] = sh.best[tid];
+            if (tid == 0) sh.ncand = nbest;
+            __syncthreads();
+        }
     }
 
-    // ---- publish ----
-    storage* out_v = static_cast<storage*>(a.out_values) + c * k;
-    int32_t* out_i = a.out_ids + c * k;
-    if (a.S == 1) {
-        if (tid < k) {
-            const uint64_t key = sh.best[tid];
-            const uint32_t row = key_row(key), o = key_order(key);
-            out_v[tid] = (storage)((o == DT::kZeroOrder || o == DT::kNanOrder) ? (uint32_t)col[row]
-                                                                               : DT::bits_from_order(o));
-            out_i[tid] = (int32_t)row;
-        }
-        return;
-    }
+    // ---- publish the segment's sorted list, then take the column's ticket ----
     const uint64_t sentinel = tag;  // order 0: below every real key
-    uint64_t* col_parts = a.partials + c * a.S * (int64_t)k;
-    if (tid < k)
-        __hip_atomic_store(&col_parts[s * k + tid], tid < nbest ? sh.best[tid] : sentinel,
+    uint64_t* parts = a.partials + (int64_t)c * S * k;
+    if (tid < k)  // wave 0 (k <= 64): the stores precede the ticket in program order
+        __hip_atomic_store(&parts[s * k + tid], tid < nbest ? sh.best[tid] : sentinel,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (tid == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(&a.tickets[c], 1u, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        sh.is_last = old == (uint32_t)(a.S - 1) ? 1u : 0u;
+        const uint32_t old = __hip_atomic_fetch_add(&a.tickets[c * kTicketStride], 1u,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sh.is_last = old == S - 1u ? 1u : 0u;
     }
     __syncthreads();
     if (!sh.is_last) return;
 
-    // ---- last workgroup of the column: merge the S lists ----
-    const uint32_t total = (uint32_t)a.S * k;
-    uint64_t keys[kMergeKeysPerThread];
-#pragma unroll
-    for (int j = 0; j < kMergeKeysPerThread; ++j) {
-        const uint32_t idx = tid + (uint32_t)j * kBlock;
-        keys[j] = 0;
-        if (idx < total) {
-            const uint32_t seg = idx / k, slot = idx - seg * k;
-            if ((int64_t)seg == s) keys[j] = slot < nbest ? sh.best[slot] : sentinel;
-            else keys[j] = load_published(&col_parts[idx]);
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < kMergeKeysPerThread; ++j) {
-        const uint32_t idx = tid + (uint32_t)j * kBlock;
-        if (idx < total) {
-            for (int spin = 0; key_tag(keys[j]) != tag && spin < kSpinLimit; ++spin) {
-                __builtin_amdgcn_s_sleep(1);
-                keys[j] = load_published(&col_parts[idx]);
-            }
-        }
-    }
-    uint64_t rep = 0;
-#pragma unroll
-    for (int j = 0; j < kMergeKeysPerThread; ++j) rep = max(rep, keys[j]);
-    const uint32_t wt = wave_kth_largest<OB>(key_order(rep), k);
-    if (lane == 0) sh.wave_thr[wave] = wt;
-    if (tid == 0) sh.cnt = 0;
-    __syncthreads();
-    uint32_t T = sh.wave_thr[0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) T = max(T, sh.wave_thr[w]);
-#pragma unroll
-    for (int j = 0; j < kMergeKeysPerThread; ++j)
-        if (keys[j] != 0 && key_order(keys[j]) >= T) append(sh, keys[j]);
-    __syncthreads();
-    const uint32_t cnt = sh.cnt;
-    if (cnt > (uint32_t)kCandCap) {
-        auto visit = [&](auto&& f) {
-#pragma unroll
-            for (int j = 0; j < kMergeKeysPerThread; ++j)
-                if (keys[j] != 0) f(keys[j]);
-        };
-        exact_topk<OB>(sh, visit, k, phase);
-    } else {
-        rank_select(sh.cand, cnt, k, sh.best);
-        __syncthreads();
-    }
+    // ---- the column's last workgroup: select from the S published lists ----
+    merge_lists<DT>(a, sh, parts);
     if (tid < k) {
         const uint64_t key = sh.best[tid];
         const uint32_t row = key_row(key), o = key_order(key);
-        out_v[tid] = (storage)((o == DT::kZeroOrder || o == DT::kNanOrder) ? (uint32_t)col[row]
-                                                                           : DT::bits_from_order(o));
-        out_i[tid] = (int32_t)row;
+        static_cast<storage*>(a.out_values)[(int64_t)c * k + tid] =
+            (storage)((o == DT::kZeroOrder || o == DT::kNanOrder) ? (uint32_t)col[row]
+                                                                  : DT::bits_from_order(o));
+        a.out_ids[(int64_t)c * k + tid] = (int32_t)row;
     }
-    if (tid == 0) __hip_atomic_store(&a.tickets[c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0)
+        __hip_atomic_store(&a.tickets[c * kTicketStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <class DT>
+hipError_t launch_dt(int nv, const ColArgs& a, hipStream_t stream) {
+    const dim3 grid((uint32_t)((int64_t)a.C * a.S)), block(kBlock);
+    switch (nv) {
+        case 2: hipLaunchKernelGGL((topk_col_kernel<DT, 2>), grid, block, 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((topk_col_kernel<DT, 4>), grid, block, 0, stream, a); break;
+        case 8: hipLaunchKernelGGL((topk_col_kernel<DT, 8>), grid, block, 0, stream, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_col_bf16(const ColArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((topk_col_kernel<Bf16, kColVecsPerThread>), dim3((uint32_t)(a.C * a.S)),
-                       dim3(kBlock), 0, stream, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_col_f32(const ColArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((topk_col_kernel<F32, kColVecsPerThread>), dim3((uint32_t)(a.C * a.S)),
-                       dim3(kBlock), 0, stream, a);
-    return hipGetLastError();
+hipError_t launch_col(int dtype, int nv, const ColArgs& a, hipStream_t stream) {
+    return dtype == 0 ? launch_dt<Bf16>(nv, a, stream) : launch_dt<F32>(nv, a, stream);
 }
 
 }  // namespace topk

@@ -17,7 +17,8 @@ struct topk_cols {
     int device;
     int64_t segments;   // workgroups per column
     int64_t blocks;     // workgroups of the main kernel
-    void* workspace;    // tickets then partial keys
+    int nv;             // 16-byte vectors per lane per pass
+    void* workspace;    // tickets, then the published lists (C*S*k keys)
     size_t workspace_bytes;
     uint32_t* tickets;
     uint64_t* partials;
@@ -27,10 +28,8 @@ struct topk_cols {
 namespace {
 
 constexpr int64_t kBlockThreads = 256;
-// A single pass holds this many 16-byte vectors per workgroup.
-constexpr int64_t kVecsPerPass = kBlockThreads * topk::kColVecsPerThread;
-// Workgroups the column-contiguous launch aims for: enough that every CU has
-// work even when the matrix has few columns.
+// Scan workgroups the column-contiguous launch aims for: enough that every CU
+// has work even when the matrix has few columns.
 constexpr int64_t kTargetBlocksPerCU = 2;
 // Do not split a column into segments smaller than this many vectors.
 constexpr int64_t kMinVecsPerSegment = 64;
@@ -39,17 +38,26 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int element_size(int32_t dtype) { return dtype == TOPK_BF16 ? 2 : 4; }
 
-int64_t choose_col_segments(int64_t V, int64_t C, int32_t k, int dtype, int cu_count) {
-    const int64_t per_vec = 16 / element_size(dtype);
-    const int64_t nvec = V / per_vec;
-    int64_t s = ceil_div(nvec, kVecsPerPass);                          // one pass per workgroup
+int64_t vectors_per_column(int64_t V, int dtype) { return V / (16 / element_size(dtype)); }
+
+int64_t choose_col_segments(int64_t V, int64_t C, int dtype, int cu_count) {
+    const int64_t nvec = vectors_per_column(V, dtype);
+    const int64_t max_nv = topk::kColVecChoices[2];
+    int64_t s = ceil_div(nvec, kBlockThreads * max_nv);                 // one pass per workgroup
     const int64_t fill = ceil_div((int64_t)cu_count * kTargetBlocksPerCU, C);
     if (fill > s) s = fill;
-    const int64_t most = nvec / kMinVecsPerSegment;                    // not too thin
+    const int64_t most = nvec / kMinVecsPerSegment;                     // not too thin
     if (s > most) s = most;
-    const int64_t merge_cap = topk::kMaxMergeKeys / k;
-    if (s > merge_cap) s = merge_cap;
+    if (s > topk::kMaxSegments) s = topk::kMaxSegments;
     return s < 1 ? 1 : s;
+}
+
+// Smallest vector count per lane that covers a segment in one pass.
+int choose_col_nv(int64_t V, int64_t S, int dtype) {
+    const int64_t per_block = ceil_div(vectors_per_column(V, dtype), S);
+    for (int nv : topk::kColVecChoices)
+        if (per_block <= kBlockThreads * nv) return nv;
+    return topk::kColVecChoices[2];
 }
 
 int create_impl(topk_cols_t* out, int64_t V, int64_t C, int32_t k, int32_t dtype, int32_t layout,
@@ -64,7 +72,7 @@ int create_impl(topk_cols_t* out, int64_t V, int64_t C, int32_t k, int32_t dtype
     if (forced_segments < 0) return TOPK_ERR_INVALID_ARG;
     if (k > TOPK_MAX_K || V > TOPK_MAX_V) return TOPK_ERR_UNSUPPORTED;
     if (layout == TOPK_ROW_INTERLEAVED) return TOPK_ERR_UNSUPPORTED;
-    if (forced_segments > 0 && forced_segments * k > topk::kMaxMergeKeys) return TOPK_ERR_UNSUPPORTED;
+    if (forced_segments > topk::kMaxSegments) return TOPK_ERR_UNSUPPORTED;
 
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess) return TOPK_ERR_HIP;
@@ -73,19 +81,19 @@ int create_impl(topk_cols_t* out, int64_t V, int64_t C, int32_t k, int32_t dtype
         cu_count < 1)
         return TOPK_ERR_HIP;
 
-    const int64_t S = forced_segments > 0 ? forced_segments
-                                          : choose_col_segments(V, C, k, dtype, cu_count);
+    const int64_t S = forced_segments > 0 ? forced_segments : choose_col_segments(V, C, dtype, cu_count);
     const int64_t blocks = C * S;
     if (blocks > 0x7FFFFFFF) return TOPK_ERR_UNSUPPORTED;
 
-    const size_t ticket_bytes = ((size_t)C * sizeof(uint32_t) + 255) & ~(size_t)255;
-    const size_t partial_bytes = S > 1 ? (size_t)C * (size_t)S * (size_t)k * sizeof(uint64_t) : 0;
-    const size_t ws_bytes = ticket_bytes + partial_bytes;
+    const size_t ticket_bytes =
+        ((size_t)C * topk::kTicketStride * sizeof(uint32_t) + 255) & ~(size_t)255;
+    const size_t ws_bytes = ticket_bytes + (size_t)C * (size_t)S * (size_t)k * sizeof(uint64_t);
 
     topk_cols* h = new (std::nothrow) topk_cols();
     if (!h) return TOPK_ERR_OUT_OF_MEMORY;
     h->V = V; h->C = C; h->ld = ld; h->k = k; h->dtype = dtype; h->layout = layout;
     h->device = device; h->segments = S; h->blocks = blocks;
+    h->nv = choose_col_nv(V, S, dtype);
     h->workspace_bytes = ws_bytes;
     hipError_t e = hipMalloc(&h->workspace, ws_bytes);
     if (e != hipSuccess) {
@@ -94,8 +102,7 @@ int create_impl(topk_cols_t* out, int64_t V, int64_t C, int32_t k, int32_t dtype
         return e == hipErrorOutOfMemory ? TOPK_ERR_OUT_OF_MEMORY : TOPK_ERR_HIP;
     }
     h->tickets = static_cast<uint32_t*>(h->workspace);
-    h->partials = S > 1 ? reinterpret_cast<uint64_t*>(static_cast<char*>(h->workspace) + ticket_bytes)
-                        : nullptr;
+    h->partials = reinterpret_cast<uint64_t*>(static_cast<char*>(h->workspace) + ticket_bytes);
     if (hipMemset(h->workspace, 0, ws_bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
         (void)hipFree(h->workspace);
         delete h;
@@ -139,8 +146,7 @@ int topk_cols_run(topk_cols_t h, const void* logits, void* out_values, int32_t* 
     a.tickets = h->tickets;
     a.out_values = out_values;
     a.out_ids = out_ids;
-    const hipError_t e = h->dtype == TOPK_BF16 ? topk::launch_col_bf16(a, stream)
-                                               : topk::launch_col_f32(a, stream);
+    const hipError_t e = topk::launch_col(h->dtype, h->nv, a, stream);
     if (e != hipSuccess) return TOPK_ERR_HIP;
     ++h->runs;
     return TOPK_OK;

@@ -23,11 +23,19 @@ namespace topk {
 constexpr int kBlock = 256;              // threads per workgroup (4 waves of 64)
 constexpr int kWaves = kBlock / 64;
 constexpr int kMaxK = 64;                // largest k (the wave-wide k-th search needs k <= 64)
-constexpr int kCandCap = 512;            // LDS candidate slots per workgroup
 constexpr uint32_t kMaxRow = 0xFFFFFFu;  // rows must fit in 24 bits
 
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Typed minimum/maximum.  (The generic max/min overloads can resolve mixed
+// 64-bit integer arguments to the double-precision versions, which is slow
+// and rounds 64-bit keys.)
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t max_u32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t min_u32(uint32_t a, uint32_t b) { return a < b ? a : b; }
+__device__ __forceinline__ int max_i32(int a, int b) { return a > b ? a : b; }
+__device__ __forceinline__ int min_i32(int a, int b) { return a < b ? a : b; }
 
 // ------------------------------------------------------------------ keys ---
 
@@ -138,36 +146,87 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
     return v;
 }
 
-// ------------------------------------------------------ block primitives ---
-
-// Rank selection: cand[0..cnt) are distinct keys in LDS.  The key of rank r
-// (r < k, rank 0 = largest) is written to best[r].  Each key's rank is the
-// number of keys above it; every lane of a wave reads the same cand[j], so
-// the LDS reads are broadcasts.
-__device__ __forceinline__ void rank_select(const uint64_t* cand, uint32_t cnt, uint32_t k,
-                                            uint64_t* best) {
-    for (uint32_t t = threadIdx.x; t < cnt; t += kBlock) {
-        const uint64_t key = cand[t];
-        uint32_t r = 0;
-        for (uint32_t j = 0; j < cnt; ++j) r += cand[j] > key ? 1u : 0u;
-        if (r < k) best[r] = key;
-    }
+// Number of lanes below this one whose bit is set in `mask`.
+__device__ __forceinline__ uint32_t lanes_below(unsigned long long mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// Block-wide count reduction: every thread contributes `local`; all threads
-// get the total.  `slot` is a 3-entry zeroed LDS array used in rotation
-// (call n uses entry n % 3), so one barrier per call suffices: after call n's
-// barrier every thread has finished reading entry (n-1) % 3, which is then
-// cleared for call n+2, whose additions come after call n+1's barrier.
-__device__ __forceinline__ uint32_t block_sum(uint32_t local, uint32_t* slot, uint32_t& phase) {
-    const uint32_t w = wave_sum(local);
-    if ((threadIdx.x & 63) == 0) atomicAdd(&slot[phase], w);
-    __syncthreads();
-    const uint32_t total = slot[phase];
-    const uint32_t stale = phase == 0 ? 2u : phase - 1u;
-    if (threadIdx.x == 0) slot[stale] = 0;
-    phase = phase == 2 ? 0u : phase + 1u;
-    return total;
+// Wave-uniform append: every lane calls it; the lanes with `has` write their
+// key to buf[cnt + (number of such lanes below)], positions at or past `cap`
+// are dropped.  Returns the new count (which may exceed cap: overflow).
+__device__ __forceinline__ uint32_t wave_append(uint64_t* buf, uint32_t cnt, uint32_t cap, bool has,
+                                                uint64_t key) {
+    const unsigned long long m = __ballot(has);
+    if (has) {
+        const uint32_t pos = cnt + lanes_below(m);
+        if (pos < cap) buf[pos] = key;
+    }
+    return cnt + (uint32_t)__popcll(m);
+}
+
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+
+// Rank selection: keys[0..n) are distinct keys in LDS (16-byte aligned,
+// readable up to n rounded up to 8).  The key of rank r (r < k, rank 0 =
+// largest) is written to out[r]; returns min(n, k).  A key's rank is the
+// number of keys above it.  Threads first, first + stride, ... take one key
+// each; all of them read the same eight keys per step with 16-byte LDS reads
+// (broadcasts), so the count is not bound by the latency of one read per key.
+__device__ __forceinline__ uint32_t rank_select(const uint64_t* keys, uint32_t n, uint32_t k,
+                                                uint64_t* out, uint32_t first, uint32_t stride) {
+    const uint32_t n8 = (n + 7u) & ~7u;
+    for (uint32_t t = first; t < n; t += stride) {
+        const uint64_t key = keys[t];
+        uint32_t r = 0;
+        for (uint32_t j = 0; j < n8; j += 8) {
+            const u64x2 q0 = *reinterpret_cast<const u64x2*>(keys + j);
+            const u64x2 q1 = *reinterpret_cast<const u64x2*>(keys + j + 2);
+            const u64x2 q2 = *reinterpret_cast<const u64x2*>(keys + j + 4);
+            const u64x2 q3 = *reinterpret_cast<const u64x2*>(keys + j + 6);
+            const uint64_t v0 = q0.x, v1 = q0.y, v2 = q1.x, v3 = q1.y;
+            const uint64_t v4 = q2.x, v5 = q2.y, v6 = q3.x, v7 = q3.y;
+            r += (v0 > key && j + 0 < n) + (v1 > key && j + 1 < n) +
+                 (v2 > key && j + 2 < n) + (v3 > key && j + 3 < n) +
+                 (v4 > key && j + 4 < n) + (v5 > key && j + 5 < n) +
+                 (v6 > key && j + 6 < n) + (v7 > key && j + 7 < n);
+        }
+        if (r < k) out[r] = key;
+    }
+    return min_u32(n, k);
+}
+
+// Rank selection by one wave (see rank_select).
+__device__ __forceinline__ uint32_t wave_rank_select(const uint64_t* keys, uint32_t n, uint32_t k,
+                                                     uint64_t* out) {
+    return rank_select(keys, n, k, out, threadIdx.x & 63u, 64u);
+}
+
+// Exact top-k of the keys a wave holds, by a bit-by-bit search for the k-th
+// largest key (the tag bits [7:0] are equal for all keys and skipped), then a
+// rank count of the at most k keys at or above it.  visit(f) calls
+// f(key, valid) for every key slot of the calling lane, in the same order on
+// every lane.  Collects into buf (cap entries), writes the result sorted to
+// out[0..n) and returns n = min(k, number of valid keys).  Valid keys must be
+// distinct.
+template <int OrderBits, class Visit>
+__device__ __forceinline__ uint32_t wave_exact_topk(uint64_t* buf, uint32_t cap, uint64_t* out,
+                                                    const Visit& visit, uint32_t k) {
+    uint32_t local = 0;
+    visit([&](uint64_t, bool valid) { local += valid ? 1u : 0u; });
+    const uint32_t total = wave_sum(local);
+    uint64_t thr = 0;
+    if (total > k) {
+        for (int b = 32 + OrderBits - 1; b >= 8; --b) {
+            const uint64_t cand = thr | (1ull << b);
+            uint32_t n = 0;
+            visit([&](uint64_t key, bool valid) { n += (valid && key >= cand) ? 1u : 0u; });
+            if (wave_sum(n) >= k) thr = cand;
+        }
+    }
+    uint32_t cnt = 0;
+    visit([&](uint64_t key, bool valid) { cnt = wave_append(buf, cnt, cap, valid && key >= thr, key); });
+    return wave_rank_select(buf, min_u32(cnt, cap), k, out);
 }
 
 }  // namespace topk

@@ -9,30 +9,33 @@ namespace topk {
 
 // Column-contiguous launch: element (r, c) at x[c*ld + r].
 // The grid is C*S workgroups; workgroup b handles column b / S and vocabulary
-// segment b % S.
+// segment b % S and publishes that segment's sorted top-k.  The last
+// workgroup of a column to finish merges the column's S lists.
 struct ColArgs {
     const void* x;
     int64_t ld;
     int64_t V;
     int32_t C;
     int32_t k;
-    int32_t S;            // vocabulary segments (workgroups) per column
+    int32_t S;            // vocabulary segments (workgroups) per column, <= kMaxSegments
     uint32_t tag;         // 1..255, differs between consecutive runs of a handle
-    uint64_t* partials;   // C*S*k keys (unused when S == 1)
-    uint32_t* tickets;    // C counters, zero between runs
+    uint64_t* partials;   // C*S*k keys: one list of k per workgroup
+    uint32_t* tickets;    // C counters kTicketStride apart, zero between runs
     void* out_values;     // C*k elements of the input dtype
     int32_t* out_ids;     // C*k
 };
 
-hipError_t launch_col_bf16(const ColArgs& a, hipStream_t stream);
-hipError_t launch_col_f32(const ColArgs& a, hipStream_t stream);
+// Waves per workgroup of the column-contiguous kernel.
+constexpr int kColWavesPerBlock = 4;
+// The last workgroup merges S*k <= 4096 keys, 16 per thread.
+constexpr int kMaxSegments = 64;
+// Per-column tickets sit 128 bytes apart: counters of different columns in
+// one cache line serialize every workgroup's atomic on that line.
+constexpr int kTicketStride = 32;
+// 16-byte vectors per lane per pass: the kernel is instantiated for these.
+constexpr int kColVecChoices[3] = {2, 4, 8};
 
-// Limit on S * k: the last workgroup of a column merges S lists of k keys,
-// at most this many, held 16 per thread.
-constexpr int kMaxMergeKeys = 4096;
-
-// Elements each thread holds per pass of the column-contiguous kernel
-// (NV 16-byte vectors per thread).
-constexpr int kColVecsPerThread = 8;
+// dtype: TOPK_BF16 or TOPK_F32; nv: one of kColVecChoices.
+hipError_t launch_col(int dtype, int nv, const ColArgs& a, hipStream_t stream);
 
 }  // namespace topk

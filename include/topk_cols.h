@@ -66,8 +66,8 @@ typedef struct topk_cols *topk_cols_t;
  * ld: leading dimension in elements, ld >= V (column-contiguous) or ld >= C
  *     (row-interleaved).  Elements in the padding are never read.
  *
- * The handle owns a small device workspace (per-block partial results and
- * per-column counters).  Create allocates it on the current device with
+ * The handle owns a small device workspace: one partial list per
+ * workgroup (C * segments * k keys of 8 bytes) and one counter per column.  Create allocates it on the current device with
  * hipMalloc, zeroes it and waits for the zeroing to finish; create is not
  * meant for the hot loop.
  *
@@ -115,8 +115,8 @@ const char *topk_cols_status_string(int status);
  * Like topk_cols_create, but with the vocabulary-axis split fixed to
  * `segments` workgroups per column (row segments for the interleaved layout)
  * instead of the automatic choice; 0 means automatic.  For tests and tuning:
- * the result is the same for every split.  segments * k must not exceed 4096
- * (TOPK_ERR_UNSUPPORTED otherwise); negative values are TOPK_ERR_INVALID_ARG.
+ * the result is the same for every split.  segments above 64 return
+ * TOPK_ERR_UNSUPPORTED; negative values return TOPK_ERR_INVALID_ARG.
  */
 int topk_cols_create_with_segments(topk_cols_t *out, int64_t V, int64_t C, int32_t k,
                                    int32_t dtype, int32_t layout, int64_t ld, int64_t segments);

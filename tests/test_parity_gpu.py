@@ -143,7 +143,7 @@ def test_every_segment_count(gpu, dtype):
     x = W.random_matrix(77, V, C, dtype, W.COL, kind="normal")
     for k in (1, 8, 64):
         for seg in (1, 2, 3, 7, 16, 31, 64):
-            if seg * k > 4096:
+            if seg > 64:
                 continue
             print(f"[parity] segments={seg} k={k} {dtype}", flush=True)
             assert_parity(gpu, x, V, C, k, dtype, W.COL, V, segments=seg, label=f"segments={seg} k={k}")
