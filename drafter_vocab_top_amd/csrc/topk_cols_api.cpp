@@ -17,7 +17,8 @@ struct topk_cols {
     int device;
     int64_t segments;   // workgroups per column
     int64_t blocks;     // workgroups of the main kernel
-    int nv;             // 16-byte vectors per lane per pass
+    int64_t tiles;      // column tiles (row-interleaved layout)
+    int nv;             // 16-byte vectors (row steps) per lane per pass
     void* workspace;    // tickets, then the published lists (C*S*k keys)
     size_t workspace_bytes;
     uint32_t* tickets;
@@ -52,6 +53,26 @@ int64_t choose_col_segments(int64_t V, int64_t C, int dtype, int cu_count) {
     return s < 1 ? 1 : s;
 }
 
+// Row-interleaved: tiles of 128 bytes of a row; row segments so that about
+// kTargetBlocksPerCU workgroups run per CU, each segment at least one
+// 32-row step, and the merge input S*k within its limit.
+int64_t choose_row_segments(int64_t V, int64_t tiles, int32_t k, int cu_count) {
+    int64_t s = ceil_div((int64_t)cu_count * kTargetBlocksPerCU, tiles);
+    const int64_t most_rows = V / 32;
+    if (s > most_rows) s = most_rows;
+    const int64_t merge_cap = topk::kRowMaxMergeKeys / k;
+    if (s > merge_cap) s = merge_cap;
+    return s < 1 ? 1 : s;
+}
+
+// Row steps of 32 rows per pass: the smallest of 2/4/8 that covers a segment.
+int choose_row_nv(int64_t V, int64_t S) {
+    const int64_t rows = ceil_div(V, S);
+    for (int nv : topk::kColVecChoices)
+        if (rows <= 32 * nv) return nv;
+    return topk::kColVecChoices[2];
+}
+
 // Smallest vector count per lane that covers a segment in one pass.
 int choose_col_nv(int64_t V, int64_t S, int dtype) {
     const int64_t per_block = ceil_div(vectors_per_column(V, dtype), S);
@@ -71,8 +92,9 @@ int create_impl(topk_cols_t* out, int64_t V, int64_t C, int32_t k, int32_t dtype
     if (layout == TOPK_ROW_INTERLEAVED && ld < C) return TOPK_ERR_INVALID_ARG;
     if (forced_segments < 0) return TOPK_ERR_INVALID_ARG;
     if (k > TOPK_MAX_K || V > TOPK_MAX_V) return TOPK_ERR_UNSUPPORTED;
-    if (layout == TOPK_ROW_INTERLEAVED) return TOPK_ERR_UNSUPPORTED;
     if (forced_segments > topk::kMaxSegments) return TOPK_ERR_UNSUPPORTED;
+    const bool row = layout == TOPK_ROW_INTERLEAVED;
+    if (row && forced_segments * k > topk::kRowMaxMergeKeys) return TOPK_ERR_UNSUPPORTED;
 
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess) return TOPK_ERR_HIP;
@@ -81,19 +103,22 @@ int create_impl(topk_cols_t* out, int64_t V, int64_t C, int32_t k, int32_t dtype
         cu_count < 1)
         return TOPK_ERR_HIP;
 
-    const int64_t S = forced_segments > 0 ? forced_segments : choose_col_segments(V, C, dtype, cu_count);
-    const int64_t blocks = C * S;
+    const int64_t tiles = row ? ceil_div(C, topk::row_tile_columns(dtype)) : 0;
+    const int64_t S = forced_segments > 0 ? forced_segments
+                      : row ? choose_row_segments(V, tiles, k, cu_count)
+                            : choose_col_segments(V, C, dtype, cu_count);
+    const int64_t blocks = row ? tiles * S : C * S;
     if (blocks > 0x7FFFFFFF) return TOPK_ERR_UNSUPPORTED;
 
     const size_t ticket_bytes =
-        ((size_t)C * topk::kTicketStride * sizeof(uint32_t) + 255) & ~(size_t)255;
+        row ? 0 : ((size_t)C * topk::kTicketStride * sizeof(uint32_t) + 255) & ~(size_t)255;
     const size_t ws_bytes = ticket_bytes + (size_t)C * (size_t)S * (size_t)k * sizeof(uint64_t);
 
     topk_cols* h = new (std::nothrow) topk_cols();
     if (!h) return TOPK_ERR_OUT_OF_MEMORY;
     h->V = V; h->C = C; h->ld = ld; h->k = k; h->dtype = dtype; h->layout = layout;
-    h->device = device; h->segments = S; h->blocks = blocks;
-    h->nv = choose_col_nv(V, S, dtype);
+    h->device = device; h->segments = S; h->blocks = blocks; h->tiles = tiles;
+    h->nv = row ? choose_row_nv(V, S) : choose_col_nv(V, S, dtype);
     h->workspace_bytes = ws_bytes;
     hipError_t e = hipMalloc(&h->workspace, ws_bytes);
     if (e != hipSuccess) {
@@ -101,7 +126,7 @@ int create_impl(topk_cols_t* out, int64_t V, int64_t C, int32_t k, int32_t dtype
         delete h;
         return e == hipErrorOutOfMemory ? TOPK_ERR_OUT_OF_MEMORY : TOPK_ERR_HIP;
     }
-    h->tickets = static_cast<uint32_t*>(h->workspace);
+    h->tickets = row ? nullptr : static_cast<uint32_t*>(h->workspace);
     h->partials = reinterpret_cast<uint64_t*>(static_cast<char*>(h->workspace) + ticket_bytes);
     if (hipMemset(h->workspace, 0, ws_bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
         (void)hipFree(h->workspace);
@@ -134,19 +159,36 @@ int topk_cols_run(topk_cols_t h, const void* logits, void* out_values, int32_t* 
         ((uintptr_t)out_ids % 4) != 0)
         return TOPK_ERR_INVALID_ARG;
 
-    topk::ColArgs a;
-    a.x = logits;
-    a.ld = h->ld;
-    a.V = h->V;
-    a.C = (int32_t)h->C;
-    a.k = h->k;
-    a.S = (int32_t)h->segments;
-    a.tag = 1u + (h->runs % 255u);
-    a.partials = h->partials;
-    a.tickets = h->tickets;
-    a.out_values = out_values;
-    a.out_ids = out_ids;
-    const hipError_t e = topk::launch_col(h->dtype, h->nv, a, stream);
+    hipError_t e;
+    if (h->layout == TOPK_ROW_INTERLEAVED) {
+        topk::RowArgs a;
+        a.x = logits;
+        a.ld = h->ld;
+        a.V = h->V;
+        a.C = (int32_t)h->C;
+        a.k = h->k;
+        a.S = (int32_t)h->segments;
+        a.tiles = (int32_t)h->tiles;
+        a.vec_loads = ((uintptr_t)logits % 16 == 0 && (h->ld * (int64_t)es) % 16 == 0) ? 1 : 0;
+        a.partials = h->partials;
+        a.out_values = out_values;
+        a.out_ids = out_ids;
+        e = topk::launch_row(h->dtype, h->nv, a, stream);
+    } else {
+        topk::ColArgs a;
+        a.x = logits;
+        a.ld = h->ld;
+        a.V = h->V;
+        a.C = (int32_t)h->C;
+        a.k = h->k;
+        a.S = (int32_t)h->segments;
+        a.tag = 1u + (h->runs % 255u);
+        a.partials = h->partials;
+        a.tickets = h->tickets;
+        a.out_values = out_values;
+        a.out_ids = out_ids;
+        e = topk::launch_col(h->dtype, h->nv, a, stream);
+    }
     if (e != hipSuccess) return TOPK_ERR_HIP;
     ++h->runs;
     return TOPK_OK;

@@ -38,4 +38,28 @@ constexpr int kColVecChoices[3] = {2, 4, 8};
 // dtype: TOPK_BF16 or TOPK_F32; nv: one of kColVecChoices.
 hipError_t launch_col(int dtype, int nv, const ColArgs& a, hipStream_t stream);
 
+// Row-interleaved launch: element (r, c) at x[r*ld + c].  The scan grid is
+// tiles*S workgroups: workgroup b handles row segment b / tiles and column
+// tile b % tiles (128 bytes of each row); a second kernel merges each
+// column's S partial lists.
+struct RowArgs {
+    const void* x;
+    int64_t ld;
+    int64_t V;
+    int32_t C;
+    int32_t k;
+    int32_t S;            // row segments; S*k <= kRowMaxMergeKeys
+    int32_t tiles;        // column tiles
+    int32_t vec_loads;    // 1 if every row start of a tile is 16-byte aligned
+    uint64_t* partials;   // C*S*k keys
+    void* out_values;     // C*k elements of the input dtype
+    int32_t* out_ids;     // C*k
+};
+
+constexpr int kRowMaxMergeKeys = 1024;
+
+// Columns per tile for a dtype (128 bytes of a row).
+int row_tile_columns(int dtype);
+hipError_t launch_row(int dtype, int nv, const RowArgs& a, hipStream_t stream);
+
 }  // namespace topk

@@ -66,10 +66,11 @@ typedef struct topk_cols *topk_cols_t;
  * ld: leading dimension in elements, ld >= V (column-contiguous) or ld >= C
  *     (row-interleaved).  Elements in the padding are never read.
  *
- * The handle owns a small device workspace: one partial list per
- * workgroup (C * segments * k keys of 8 bytes) and one counter per column.  Create allocates it on the current device with
- * hipMalloc, zeroes it and waits for the zeroing to finish; create is not
- * meant for the hot loop.
+ * The handle owns a small device workspace: one partial list of k 8-byte
+ * keys per column and vocabulary segment (C * segments * k keys) and, for the
+ * column-contiguous layout, one 128-byte counter line per column.  Create
+ * allocates it on the current device with hipMalloc, zeroes it and waits for
+ * the zeroing to finish; create is not meant for the hot loop.
  *
  * On any failure *out is set to NULL, and nothing stays allocated.
  * Returns TOPK_ERR_INVALID_ARG for a bad argument or a NULL out.
@@ -115,7 +116,8 @@ const char *topk_cols_status_string(int status);
  * Like topk_cols_create, but with the vocabulary-axis split fixed to
  * `segments` workgroups per column (row segments for the interleaved layout)
  * instead of the automatic choice; 0 means automatic.  For tests and tuning:
- * the result is the same for every split.  segments above 64 return
+ * the result is the same for every split.  segments above 64, or (for the
+ * row-interleaved layout) segments * k above 1024, return
  * TOPK_ERR_UNSUPPORTED; negative values return TOPK_ERR_INVALID_ARG.
  */
 int topk_cols_create_with_segments(topk_cols_t *out, int64_t V, int64_t C, int32_t k,
@@ -126,7 +128,8 @@ int topk_cols_create_with_segments(topk_cols_t *out, int64_t V, int64_t C, int32
  * chosen at create.
  * segments: workgroups per column (vocabulary-axis split) for the
  *           column-contiguous kernel, or row segments for the interleaved one.
- * blocks: total workgroups of the main kernel.
+ * blocks: total workgroups of the scan kernel (the row-interleaved layout
+ *         adds a merge kernel of ceil(C / 4) workgroups).
  * workspace_bytes: device bytes owned by the handle.
  * Any output pointer may be NULL.
  */

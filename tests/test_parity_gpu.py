@@ -1,4 +1,5 @@
-"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+"""GPU parity of the column-contiguous layout, and of the seeded workloads in
+both layouts: the HIP library (through its C ABI) against the CPU oracle.
 
 The bar is bit-exact.  Output values are compared as raw bits and ids as
 integers.  Every GPU output is also checked against the invariants in
@@ -13,89 +14,31 @@ import hashlib
 import numpy as np
 import pytest
 
-import oracle
 from drafter_vocab_top_amd import workloads as W
-from topk_checks import bits, check_invariants, golden_names, read_golden
+from gpu_harness import assert_parity, run_gpu, run_oracle, to_device
+from topk_checks import bits, golden_names, read_golden
 
 pytestmark = pytest.mark.gpu
-
-ODT = {W.BF16: oracle.BF16, W.F32: oracle.F32}
-OLY = {W.COL: oracle.COL_CONTIG, W.ROW: oracle.ROW_INTERLEAVED}
-
-
-@pytest.fixture(scope="module")
-def gpu():
-    import torch
-    if not torch.cuda.is_available():
-        pytest.skip("no GPU")
-    from drafter_vocab_top_amd import topk_cols as T
-    T.load()   # fails loudly if the library is missing
-    return torch, T
-
-
-def to_device(torch, x, offset=0):
-    """Copy a storage array to the GPU, starting `offset` elements into a fresh
-    buffer (offset > 0 gives a column base that is not 16-byte aligned)."""
-    flat = np.ascontiguousarray(x).reshape(-1)
-    if flat.dtype == np.uint16:
-        host = torch.from_numpy(flat.view(np.int16))
-    else:
-        host = torch.from_numpy(flat.view(np.int32))
-    buf = torch.empty(flat.size + offset + 8, dtype=host.dtype, device="cuda")
-    buf.fill_(0x7F7F if flat.dtype == np.uint16 else 0x7F7FFFFF)
-    buf[offset:offset + flat.size].copy_(host)
-    return buf[offset:offset + flat.size]
-
-
-def run_gpu(gpu, x, V, C, k, dtype, layout, ld, segments=0, offset=0, repeat=1):
-    torch, T = gpu
-    dx = to_device(torch, x, offset)
-    with T.TopkCols(V, C, k, dtype, layout, ld, segments=segments) as h:
-        for _ in range(repeat):
-            v, i = h.run(dx)
-        torch.cuda.synchronize()
-    st = np.uint16 if dtype == W.BF16 else np.uint32
-    return v.cpu().numpy().view(st).reshape(C, k), i.cpu().numpy().reshape(C, k)
-
-
-def run_oracle(x, V, C, k, dtype, layout, ld, nthreads=8):
-    return oracle.topk_cols(x, V, C, k, ODT[dtype], OLY[layout], ld, nthreads=nthreads)
-
-
-def assert_parity(gpu, x, V, C, k, dtype, layout, ld, segments=0, offset=0, label=""):
-    gv, gi = run_gpu(gpu, x, V, C, k, dtype, layout, ld, segments=segments, offset=offset)
-    ov, oi = run_oracle(x, V, C, k, dtype, layout, ld)
-    bad = np.flatnonzero((gi != oi).any(axis=1) | (bits(gv) != bits(ov)).any(axis=1))
-    assert bad.size == 0, (f"{label}: {bad.size} of {C} columns differ; first column {bad[0]}: "
-                           f"gpu ids {gi[bad[0]][:8]} oracle ids {oi[bad[0]][:8]}")
-    check_invariants(x, V, C, k, dtype, layout, ld, gv, gi)
-
-
-def layout_supported(layout):
-    return layout == W.COL
-
 
 # ------------------------------------------------------------ fixtures ---
 
 @pytest.mark.parametrize("name", golden_names())
 def test_golden_fixtures(gpu, name):
     g = read_golden(name)
-    if not layout_supported(g["layout"]):
-        pytest.skip("row-interleaved kernel not in this build")
     gv, gi = run_gpu(gpu, g["x"], g["V"], g["C"], g["k"], g["dtype"], g["layout"], g["ld"])
     assert np.array_equal(bits(gv), g["values"]) and np.array_equal(gi, g["ids"])
 
 
 # ------------------------------------------------- full-size workloads ---
 
-@pytest.mark.parametrize("n", [1, 2, 3, 4])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
 def test_workload_full_size(gpu, n):
     w = W.config(n)
     print(f"[parity] workload {w.name} seed {w.seed}", flush=True)
     assert_parity(gpu, w.x, w.V, w.C, w.k, w.dtype, w.layout, w.ld, label=w.name)
 
 
-@pytest.mark.parametrize("n", [2, 3, 4])
+@pytest.mark.parametrize("n", [2, 3, 4, 5])
 def test_workload_other_seeds(gpu, n):
     for seed in (2000 + n, 2001 + n):
         w = W.config(n, seed=seed)

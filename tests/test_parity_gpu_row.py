@@ -1,0 +1,99 @@
+"""GPU parity of the row-interleaved layout (element (r, c) at x[r*ld + c]):
+the HIP library through its C ABI against the CPU oracle, bit-exact.
+
+The cases cover partial column tiles (C not a multiple of the 128-byte tile),
+padded and unaligned rows (element loads instead of 16-byte loads), ragged
+row segments, every split of the vocabulary axis the merge accepts, ties that
+overflow the candidate buffers (the exact fallback), and special values.
+"""
+import numpy as np
+import pytest
+
+from drafter_vocab_top_amd import workloads as W
+from gpu_harness import assert_parity
+
+pytestmark = pytest.mark.gpu
+
+
+def test_full_width_padded_and_misaligned(gpu):
+    """448 columns over a shorter vocabulary: a padded ld that keeps rows
+    16-byte aligned, one that does not, and unaligned bases."""
+    V, C, k = 60001, 448, 16
+    for ld in (456, 451):
+        x = W.random_matrix(31 + ld, V, C, W.BF16, W.ROW, ld=ld, kind="normal")
+        for offset in (0, 1, 3):
+            print(f"[parity-row] ld={ld} offset={offset}", flush=True)
+            assert_parity(gpu, x, V, C, k, W.BF16, W.ROW, ld, offset=offset,
+                          label=f"row ld={ld} offset={offset}")
+
+
+SMALL_V = [1, 2, 7, 31, 32, 33, 63, 64, 65, 255, 257, 2049, 20011]
+SMALL_C = [1, 5, 8, 33, 64, 65, 130]
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+@pytest.mark.parametrize("kind", ["normal", "alphabet", "special"])
+def test_small_sweep(gpu, dtype, kind):
+    for V in SMALL_V:
+        for C in SMALL_C:
+            for k in sorted({1, 8, 64, V}):
+                if k > V or k > 64:
+                    continue
+                x = W.random_matrix(V * 257 + C * 7 + k, V, C, dtype, W.ROW, kind=kind)
+                print(f"[parity-row] small V={V} C={C} k={k} {dtype} {kind}", flush=True)
+                assert_parity(gpu, x, V, C, k, dtype, W.ROW, C, label=f"row V={V} C={C} k={k} {kind}")
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+def test_every_segment_count(gpu, dtype):
+    """Any split of the rows gives the same answer (S*k <= 1024)."""
+    V, C = 50021, 70
+    x = W.random_matrix(78, V, C, dtype, W.ROW, kind="normal")
+    for k in (1, 16, 64):
+        for seg in (1, 2, 3, 7, 16, 31, 64):
+            if seg * k > 1024:
+                continue
+            print(f"[parity-row] segments={seg} k={k} {dtype}", flush=True)
+            assert_parity(gpu, x, V, C, k, dtype, W.ROW, C, segments=seg, label=f"row segments={seg} k={k}")
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+@pytest.mark.parametrize("kind", ["equal", "asc", "desc", "alphabet"])
+def test_ties_and_monotone_columns(gpu, dtype, kind):
+    """All-equal columns overflow every candidate buffer (exact fallback);
+    monotone columns move the running threshold at every pass."""
+    V, C = 8000, 70
+    x = W.random_matrix(6, V, C, dtype, W.ROW, kind=kind)
+    for k in (1, 16, 64):
+        for seg in (0, 1, 5):
+            print(f"[parity-row] {kind} k={k} segments={seg} {dtype}", flush=True)
+            assert_parity(gpu, x, V, C, k, dtype, W.ROW, C, segments=seg, label=f"row {kind} k={k} seg={seg}")
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+def test_negative_and_nan_columns(gpu, dtype):
+    V, C = 20000, 40
+    rng = np.random.default_rng(10)
+    base = (-10.0 + 3.0 * rng.standard_normal((V, C))).astype(np.float32)
+    b = W.bf16_bits_from_f32(base) if dtype == W.BF16 else base.view(np.uint32).copy()
+    nan_neg = 0xFFC0 if dtype == W.BF16 else 0xFFC00000
+    nan_pos = 0x7FC0 if dtype == W.BF16 else 0x7FC00000
+    for c in range(0, C, 3):
+        b[rng.choice(V, 5, replace=False), c] = nan_neg
+    for c in range(1, C, 3):
+        b[rng.choice(V, 40, replace=False), c] = nan_pos
+        b[rng.choice(V, 40, replace=False), c] = nan_neg
+    x = W.storage_from_bits(b, dtype)
+    for k in (1, 8, 64):
+        for seg in (0, 1, 4):
+            print(f"[parity-row] neg/nan k={k} segments={seg} {dtype}", flush=True)
+            assert_parity(gpu, x, V, C, k, dtype, W.ROW, C, segments=seg, label=f"row neg/nan k={k} seg={seg}")
+
+
+def test_exhaustive_small_alphabet_rows(gpu):
+    # Every length-6 column over {-inf, -1, -0, +0, 1}, stored as 6 rows of 15,625 columns.
+    cols = W.exhaustive_columns([0xFF80, 0xBF80, 0x8000, 0x0000, 0x3F80], 6).astype(np.uint16)
+    n = cols.shape[0]
+    x = np.ascontiguousarray(cols.T)
+    for k in range(1, 7):
+        assert_parity(gpu, x, 6, n, k, W.BF16, W.ROW, n, label=f"row exhaustive k={k}")
