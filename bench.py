@@ -16,10 +16,9 @@ The script prints one JSON line on stdout.  Progress goes to stderr.
                        calls between two events on the launch stream, divided
                        by K.
   roofline             algorithmic bytes per launch (every element read once
-                       plus the outputs written), divided by the kernel's mean
-                       duration.  The duration comes from an event pair around
-                       each of K calls on the same stream.  Peak is 8 TB/s
-                       HBM3E.  traffic is the HBM bytes per launch measured by
+                       plus the outputs written), divided by the mean launch
+                       duration over the timed region (the same K calls and
+                       events as value).  Peak is 8 TB/s HBM3E.  traffic is the HBM bytes per launch measured by
                        rocprofv3 counters, scaled by a plain copy of known
                        size (profiles/*_traffic.json).  It is null when the
                        kernel source changed after the counters were taken.
@@ -36,6 +35,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import statistics
 import sys
 import time
@@ -45,6 +45,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, AMD's published peak
 ROTATE_BYTES = 1 << 30          # > 4x the 256 MB Infinity Cache
+COPY_BYTES = 256 << 20          # plain copy that calibrates the HBM byte counters
 HEADLINE = 2                    # 248,046 x 7, k = 8, bf16, column-contiguous
 METRIC = "top-k us/round and HBM GB/s (% peak) at V=248,046, C=7 and C=56"
 
@@ -53,10 +54,13 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_sources_digest() -> str:
+def kernel_sources_digest(layout: str = "col") -> str:
+    """Digest of the sources that decide what the kernel of one layout does."""
     from drafter_vocab_top_amd import build as B
+    kernel = "topk_col.hip" if layout == "col" else "topk_row.hip"
+    names = (kernel, "topk_device.hpp", "topk_cols_api.cpp")
     h = hashlib.sha256()
-    for p in sorted(B.SOURCES + B.HEADERS):
+    for p in sorted(p for p in B.SOURCES + B.HEADERS if os.path.basename(p) in names):
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -232,8 +236,70 @@ def device_info(torch):
     return info
 
 
-def traffic_record(digest, config_n):
-    path = os.path.join(ROOT, "profiles", f"topk_col_cfg{config_n}_traffic.json")
+def traffic_path(w, config_n):
+    kind = "col" if w.layout == "col" else "row"
+    return os.path.join(ROOT, "profiles", f"topk_{kind}_cfg{config_n}_traffic.json")
+
+
+def _counter_rows(directory, counter):
+    """{(kernel name, dispatch id): value} from the csv files of a rocprofv3 run."""
+    import csv
+    rows = {}
+    for root, _, files in os.walk(directory):
+        for fn in files:
+            if not fn.endswith("counter_collection.csv"):
+                continue
+            with open(os.path.join(root, fn), newline="") as f:
+                for rec in csv.DictReader(f):
+                    if rec.get("Counter_Name") != counter:
+                        continue
+                    key = (rec.get("Kernel_Name", ""), int(rec.get("Dispatch_Id", "0")))
+                    rows[key] = rows.get(key, 0.0) + float(rec["Counter_Value"])
+    return rows
+
+
+def summarize_counters(fetch_dir, write_dir, config_n):
+    """HBM bytes per launch of the top-k kernels from FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch), each scaled by what the same counter reads for the
+    calibration copy of COPY_BYTES that ends a '--profile' run (the last five
+    copy dispatches; the copy reads and writes COPY_BYTES once)."""
+    from drafter_vocab_top_amd import workloads as W
+    w = W.config(config_n)
+    out = {"workload": w.name, "kernel_sources_digest": kernel_sources_digest(w.layout),
+           "commands": [f"rocprofv3 --pmc {c} -f csv -d {d} -o run -- python3 bench.py --profile {config_n} "
+                        f"--steps 10 --warmup 2" for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir))]
+                       + [f"python3 bench.py --summarize-counters {fetch_dir} {write_dir} {config_n}"],
+           "copy_bytes": COPY_BYTES, "counters": {}}
+    per_launch = 0.0
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(d, counter)
+        copies = sorted((disp, v) for (name, disp), v in rows.items() if "copyBuffer" in name)[-5:]
+        topk = {}
+        for (name, _), v in rows.items():
+            m = re.search(r"topk_\w+(<[^()]*>)?", name)
+            if m:
+                topk.setdefault(m.group(0), []).append(v)
+        if len(copies) < 5 or not topk:
+            raise SystemExit(f"{counter}: no calibration copies or top-k dispatches under {d}")
+        copy_kib = statistics.median(v for _, v in copies)
+        scale = COPY_BYTES / (copy_kib * 1024.0)
+        kern = {name: {"dispatches": len(v), "kib_per_dispatch_median": statistics.median(v),
+                       "bytes_per_launch": statistics.median(v) * 1024.0 * scale} for name, v in topk.items()}
+        out["counters"][counter] = {"copy_kib_per_dispatch": copy_kib, "scale": scale, "kernels": kern}
+        per_launch += sum(k["bytes_per_launch"] for k in kern.values())
+    out["hbm_bytes_per_launch"] = round(per_launch)
+    out["algorithmic_bytes"] = algorithmic_bytes(w)
+    out["ratio_to_algorithmic"] = per_launch / out["algorithmic_bytes"]
+    path = traffic_path(w, config_n)
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+    log(f"wrote {path}")
+
+
+def traffic_record(digest, w, config_n):
+    path = traffic_path(w, config_n)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -251,13 +317,23 @@ def main():
     ap.add_argument("--configs", default="1,2,3,4,5",
                     help="workloads measured for per_config (the headline is always measured)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile", action="store_true",
-                    help="profiling run: headline workload only, few steps, plus a copy of known size")
+    ap.add_argument("--profile", type=int, nargs="?", const=HEADLINE, default=None, metavar="N",
+                    help="profiling run: workload N only (default: the headline), few steps, "
+                         "plus a plain copy of known size")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "N"),
+                    help="turn the counter_collection.csv files of a FETCH_SIZE and a WRITE_SIZE "
+                         "rocprofv3 run of '--profile N' into profiles/topk_*_cfgN_traffic.json")
     args = ap.parse_args()
+
+    if args.summarize_counters:
+        fetch_dir, write_dir, n = args.summarize_counters
+        summarize_counters(fetch_dir, write_dir, int(n))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this path has no multi-GPU mode "
-              "(columns are independent; see DESIGN.md for how it would shard).", file=sys.stderr)
+              "(columns are independent: several GPUs would each take a share of the columns).",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -269,18 +345,18 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     T.load()
-    digest = kernel_sources_digest()
 
-    if args.profile:
-        w = W.config(HEADLINE)
+    if args.profile is not None:
+        w = W.config(args.profile)
         res = time_config(torch, T, w, args.steps, args.warmup, warm=False)
         # a plain copy of known size, for scaling the traffic counters
-        src = torch.empty(64 << 20, dtype=torch.int32, device="cuda").fill_(1)
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.int32, device="cuda").fill_(1)
         dst = torch.empty_like(src)
         for _ in range(5):
             dst.copy_(src)
         torch.cuda.synchronize()
-        log(f"profile run: {w.name} {res['us_per_round']:.2f} us/round; copy of {src.numel() * 4} bytes x5")
+        log(f"profile run: {w.name} {res['us_per_round']:.2f} us/round "
+            f"(per call mean {res['per_call_mean_us']:.2f} us); copy of {COPY_BYTES} bytes x5")
         return
 
     log(f"device: {device_info(torch)}")
@@ -329,9 +405,10 @@ def main():
             headline = (w, r)
 
     w, r = headline
-    traffic = traffic_record(digest, HEADLINE)
+    digest = kernel_sources_digest(w.layout)
+    traffic = traffic_record(digest, w, HEADLINE)
     b = algorithmic_bytes(w)
-    achieved = b / (r["per_call_mean_us"] * 1e3)
+    achieved = b / (r["us_per_round"] * 1e3)
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle (cpu_baseline) ...")
@@ -349,13 +426,14 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "u64",
-        "data": "synthetic (seeded, BASELINE.json configs; inputs resident in HBM, rotated over >=1 GiB)",
+        "data": "synthetic (seeded logits of the drafter's shapes; inputs resident in HBM, rotated over >=1 GiB)",
         "config": {"workload": w.name, "V": w.V, "C": w.C, "k": w.k, "input_dtype": w.dtype,
                    "layout": w.layout, "ld": w.ld, "segments": r["decomposition"]["segments"],
                    "blocks": r["decomposition"]["blocks"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
-                     "algorithmic_bytes": b, "kernel_mean_us": r["per_call_mean_us"]},
+                     "algorithmic_bytes": b, "kernel_mean_us": r["us_per_round"],
+                     "kernel": "topk_col_kernel" if w.layout == "col" else "topk_row_scan + topk_row_merge"},
         "cpu_baseline": cpu,
         "launch_floor_us": floor_us,
         "per_config": per_config,
