@@ -65,12 +65,9 @@ int64_t choose_row_segments(int64_t V, int64_t tiles, int32_t k, int cu_count) {
     return s < 1 ? 1 : s;
 }
 
-// Row steps of 32 rows per pass: the smallest of 2/4/8 that covers a segment.
+// Row steps of 32 rows per pass: 16 (512 rows) unless a segment is shorter.
 int choose_row_nv(int64_t V, int64_t S) {
-    const int64_t rows = ceil_div(V, S);
-    for (int nv : topk::kColVecChoices)
-        if (rows <= 32 * nv) return nv;
-    return topk::kColVecChoices[2];
+    return ceil_div(V, S) <= 256 ? 8 : 16;
 }
 
 // Smallest vector count per lane that covers a segment in one pass.

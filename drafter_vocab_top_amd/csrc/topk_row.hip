@@ -1,35 +1,49 @@
 // Row-interleaved top-k kernels for gfx950: element (r, c) at x[r*ld + c].
 //
-// This layout holds many independent rounds side by side: the column of each
-// draft position is spread over V rows ld elements apart, and one 128-byte
-// cache line holds 128 bytes of adjacent columns of one row.  Coalesced
-// reads therefore see many columns at once, so a workgroup owns a tile of
+// This layout holds many independent rounds side by side.  Each column (one
+// draft position of one round) is spread over V rows, ld elements apart, and
+// a 128-byte line holds 128 bytes of adjacent columns of one row.  Coalesced
+// reads therefore touch many columns at once.  A workgroup owns a tile of
 // columns (128 bytes of each row: 64 bf16 or 32 fp32 columns) over a segment
-// of rows, and each lane holds one 16-byte vector (8 or 4 columns) of a row
-// per load.  A wave load covers 8 rows of the tile; the workgroup, 32 rows.
-// The selection order is the same as for the column-contiguous kernel: larger
-// value first, ties to the smaller row (ignis "DFlash2" page, "How it works").
+// of rows.  Each lane loads one 16-byte vector of a row per step (8 or 4
+// columns): 8 lanes cover a row, a wave 8 rows, the workgroup 32 rows.  The
+// selection order is the one of the column-contiguous kernel: larger value
+// first, ties to the smaller row (ignis "DFlash2" page, "How it works").
 //
-// Scan kernel, one pass = NV row-steps of 32 rows:
-//  1. Per lane and column, packed 16-bit (bf16) or 32-bit integer max/min of
-//     the raw patterns over two interleaved row groups give two exact maxima
-//     (the column's order at its largest element); 32 lanes hold each column,
-//     so each column has 64 such representatives in the workgroup.
-//  2. Four threads per column bit-search the k-th largest of the 64: a lower
-//     bound on the column's k-th largest value in this pass, hence in the
-//     segment.  The column's threshold T_c is the largest bound seen so far,
-//     so it only rises.
-//  3. Elements at or above T_c are appended, as 64-bit keys, to the column's
-//     LDS buffer (a per-column LDS counter).  A lane compares its elements
-//     only for columns whose lane maximum reaches T_c.
-//  4. After the last pass each wave takes 1/4 of the tile's columns: the keys
-//     still at or above the final T_c are rank-counted to the column's exact
-//     top-k, which goes to the segment's slot of a partial list.
-// A column whose buffer overflows (massive ties) is re-read from memory by
-// one wave and selected by an exact wave-wide bit search.
+// Scan kernel.  A pass is NV steps of 32 rows, and the next pass's loads are
+// issued before the current pass is filtered.  Every column keeps a running
+// threshold T_c (an order that is at most the segment's k-th largest) and an
+// LDS buffer of candidate keys that holds every element seen so far at or
+// above T_c.
+//  1. First pass only: packed 16-bit (bf16) or 32-bit integer max/min of the
+//     raw patterns over the first two passes (both are loaded by then) give
+//     each lane two exact group maxima per column, 64 per column in the
+//     workgroup.  T_c starts as the k-th largest of them: k distinct
+//     elements are at least that large.
+//  2. Every pass: each 32-bit word of a row vector is tested against the
+//     thresholds of its columns in the raw bit domain (one xor and one packed
+//     signed max per word, see RowFilter).  A lane with a passing element
+//     appends its whole row vector to its wave's LDS queue (ballot + mbcnt).
+//     When the queue fills, and at the end of the pass, the wave turns the
+//     queued vectors into keys, one vector per lane, and adds them to the
+//     column buffers (an LDS atomic per key).
+//  3. After a pass, a column holding more than max(2k, 24) keys is trimmed:
+//     the threads of the column find the exact k-th largest order among its
+//     candidates, which becomes the new T_c, and compact the buffer in place.
+//     T_c then follows the segment's own k-th largest, so later passes add
+//     few candidates.
+//  4. At the end the same trim runs on every column, and a search over the
+//     row bits breaks ties at the k-th order: exactly k keys remain, written
+//     unsorted to the segment's slot of the partial lists.
+// A column whose buffer overflows during a pass is rebuilt at the end of the
+// pass: one wave re-reads the pass's rows of that column and keeps what is at
+// or above the exact k-th largest order seen so far.  Negative NaNs never
+// pass the raw filter; a lane notes them in a running unsigned maximum.  Such
+// a column, like one that still overflows after a rebuild (massive ties), is
+// re-read over the whole segment by one wave and selected by an exact search.
 //
-// Merge kernel: one wave per column selects the top k of its S partial
-// lists (k-th largest list maximum as threshold, then a rank count) and
+// Merge kernel: one wave per column selects the top k of its S partial lists
+// (the k-th largest of the lanes' maxima as threshold, then a rank count) and
 // writes the output.  The kernel boundary orders it after the scan.
 #include "topk_device.hpp"
 #include "topk_internal.hpp"
@@ -38,104 +52,188 @@ namespace topk {
 
 namespace {
 
-constexpr int kRowLanesPerRow = 8;                    // 8 lanes x 16 bytes = one 128-byte line
-constexpr int kRowsPerStep = kBlock / kRowLanesPerRow;  // 32 rows per workgroup load step
+constexpr int kRowLanesPerRow = 8;                      // 8 lanes x 16 bytes = one 128-byte row tile
+constexpr int kRowsPerStep = kBlock / kRowLanesPerRow;  // 32 rows per workgroup step
 constexpr int kRowTileBytes = 128;
-constexpr int kRowCap = 96;                           // candidate slots per column
-constexpr int kRowRepsPerColumn = 2 * kRowsPerStep;   // two row groups per lane
-constexpr int kRowMergeKeysPerLane = 16;              // S*k <= 1024 per column
+constexpr int kRowReps = 2 * kRowsPerStep;              // group maxima per column (first pass)
+constexpr int kRowQueue = 128;                          // queued row vectors per wave
+constexpr int kRowMergeKeysPerLane = kRowMaxMergeKeys / 64;
+// Candidate buffer per column: CAP keys.  A trim leaves about k of them and
+// is due above max(2k, 24), so a pass may add at least CAP - max(2k, 24)
+// (32 or more) before the buffer overflows.
+constexpr int kRowSmallK = 16;
+constexpr int kRowCapSmall = 64;
+constexpr int kRowCapLarge = 192;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <class DT>
-struct RowShape {
-    static constexpr int kCols = kRowTileBytes / (int)sizeof(typename DT::storage);  // tile width
-    static constexpr int kPerVec = DT::kPerVec;                                    // columns per lane
+struct RowTile {
+    static constexpr int TW = kRowTileBytes / (int)sizeof(typename DT::storage);  // columns per tile
+    static constexpr int CPV = DT::kPerVec;                                     // columns per lane
+    static constexpr int TPC = kBlock / TW;                                     // threads per column
 };
 
-template <class DT>
+template <class DT, int CAP>
 struct RowShared {
-    static constexpr int TW = RowShape<DT>::kCols;
-    alignas(16) uint64_t cand[TW][kRowCap];   // per-column candidate keys
-    alignas(16) uint64_t tmp[kWaves][kMaxK];   // per-wave selection output
-    uint32_t reps[TW][kRowRepsPerColumn + 1];  // per-pass column maxima (orders); padded row
-                                               // length spreads a column's reads over banks
-    uint32_t thr[TW];                          // running column thresholds (orders)
-    uint32_t cnt[TW];                          // candidates per column
+    static constexpr int TW = RowTile<DT>::TW;
+    static constexpr int STRIDE = CAP + 2;       // keys per column; the padding spreads LDS banks
+    alignas(16) uint64_t cand[TW][STRIDE];       // per-column candidate keys
+    alignas(16) uint64_t tmp[kWaves][kMaxK];     // exact-path output per wave
+    alignas(16) u32x4 qdata[kWaves][kRowQueue];  // queued row vectors
+    uint32_t qmeta[kWaves][kRowQueue];           // (row << 3) | lane group of each queued vector
+    uint32_t reps[TW][kRowReps + 1];             // first-pass group maxima (orders)
+    alignas(16) typename DT::storage fm[TW];     // raw-filter xor mask per column
+    alignas(16) typename DT::storage fq[TW];     // raw-filter bound per column
+    uint32_t thr[TW];                            // running threshold per column (order)
+    uint32_t cnt[TW];                            // candidates per column (may exceed CAP)
+    uint32_t flag[TW];                           // 1: candidates overflowed, 2: negative NaN seen
 };
 
 __device__ __forceinline__ s16x2 as_s16x2_r(uint32_t w) { return __builtin_bit_cast(s16x2, w); }
 __device__ __forceinline__ u16x2 as_u16x2_r(uint32_t w) { return __builtin_bit_cast(u16x2, w); }
 
-// Element j (column) of a loaded vector, j known at compile time.
+// Raw-domain test "order(x) >= T" for every pattern except negative NaNs
+// (which always fail; they are detected separately).  With y = x ^ m read as
+// a signed integer, the element passes iff y > q:
+//  - T above the zero class: m = 0 and q = (smallest positive pattern with
+//    order >= T) - 1.  Negative patterns are negative integers and fail;
+//    positive NaNs are the largest positive patterns and pass.
+//  - T at or below the zero class: the passing patterns are the unsigned
+//    range [0, R], R the negative pattern of order T (the zero class gives
+//    R = -0).  x ^ 0x7FF..F maps unsigned patterns to signed integers in
+//    decreasing order, so m = 0x7FF..F and q = (R ^ m) - 1.
+//  - T at or below the order of -Inf: every pattern but the all-ones
+//    negative NaN passes (q is the smallest signed integer).
 template <class DT>
-__device__ __forceinline__ uint32_t row_elem(const u32x4& v, int j) {
+struct RowFilter;
+
+template <>
+struct RowFilter<Bf16> {
+    __device__ __forceinline__ static void encode(uint32_t T, uint32_t& m, uint32_t& q) {
+        if (T <= 0x80u) {
+            m = 0x7FFFu;
+            q = 0x8000u;
+        } else if (T <= 0x8000u) {
+            m = 0x7FFFu;
+            q = (((0x10000u - T) ^ 0x7FFFu) - 1u) & 0xFFFFu;
+        } else if (T <= 0xFF80u) {
+            m = 0u;
+            q = T - 0x8001u;
+        } else {
+            m = 0u;
+            q = 0x7F80u;
+        }
+    }
+    // A word holds two columns; a nonzero half of the result passes.
+    __device__ __forceinline__ static uint32_t test(uint32_t x, uint32_t m, uint32_t q) {
+        const s16x2 y = as_s16x2_r(x ^ m);
+        return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(y, as_s16x2_r(q))) ^ q;
+    }
+    __device__ __forceinline__ static bool passes(uint32_t t, int half) { return ((t >> (16 * half)) & 0xFFFFu) != 0u; }
+    // running unsigned maximum of the raw patterns, per half
+    __device__ __forceinline__ static uint32_t umax(uint32_t acc, uint32_t x) {
+        return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(as_u16x2_r(acc), as_u16x2_r(x)));
+    }
+    __device__ __forceinline__ static bool has_negative_nan(uint32_t acc, int half) {
+        return ((acc >> (16 * half)) & 0xFFFFu) > 0xFF80u;
+    }
+};
+
+template <>
+struct RowFilter<F32> {
+    __device__ __forceinline__ static void encode(uint32_t T, uint32_t& m, uint32_t& q) {
+        if (T <= 0x00800000u) {
+            m = 0x7FFFFFFFu;
+            q = 0x80000000u;
+        } else if (T <= 0x80000000u) {
+            m = 0x7FFFFFFFu;
+            q = ((0u - T) ^ 0x7FFFFFFFu) - 1u;
+        } else if (T <= 0xFF800000u) {
+            m = 0u;
+            q = T - 0x80000001u;
+        } else {
+            m = 0u;
+            q = 0x7F800000u;
+        }
+    }
+    __device__ __forceinline__ static uint32_t test(uint32_t x, uint32_t m, uint32_t q) {
+        return (int)(x ^ m) > (int)q ? 1u : 0u;
+    }
+    __device__ __forceinline__ static bool passes(uint32_t t, int) { return t != 0u; }
+    __device__ __forceinline__ static uint32_t umax(uint32_t acc, uint32_t x) { return max_u32(acc, x); }
+    __device__ __forceinline__ static bool has_negative_nan(uint32_t acc, int) { return acc > 0xFF800000u; }
+};
+
+__device__ __forceinline__ uint32_t word(const u32x4& v, int q) {
+    const uint32_t wx = v.x, wy = v.y, wz = v.z, ww = v.w;
+    return q == 0 ? wx : q == 1 ? wy : q == 2 ? wz : ww;
+}
+
+// Element j (column j of the lane's vector) of a loaded vector; j may vary.
+template <class DT>
+__device__ __forceinline__ uint32_t row_elem(const u32x4& v, uint32_t j) {
     const uint32_t wx = v.x, wy = v.y, wz = v.z, ww = v.w;
     if constexpr (DT::kPerVec == 8) {
-        const uint32_t w = j < 2 ? wx : j < 4 ? wy : j < 6 ? wz : ww;
-        return (j & 1) ? (w >> 16) : (w & 0xFFFFu);
+        const uint32_t q = j >> 1;
+        const uint32_t w = q == 0 ? wx : q == 1 ? wy : q == 2 ? wz : ww;
+        return (w >> (16u * (j & 1u))) & 0xFFFFu;
     } else {
         return j == 0 ? wx : j == 1 ? wy : j == 2 ? wz : ww;
     }
 }
 
-// Exact maximum order per column of one lane over a group of rows, from the
-// raw patterns: the signed maximum when some pattern is non-negative, else the
-// signed minimum (the least negative value); any negative NaN makes it the NaN
-// class (which is the top of the order).
+// Exact maximum order per column of one lane over a group of row vectors,
+// from the raw patterns: the signed maximum when some pattern is
+// non-negative, else the signed minimum (the negative value nearest zero).
+// A negative NaN may be missed, which leaves a lower bound: enough for a
+// threshold.
 template <class DT>
 struct ColMax {
-    // bf16: two columns per packed register; fp32: one per register
-    static constexpr int R = DT::kPerVec == 8 ? 4 : 4;
-    uint32_t smax[R], smin[R], umax[R];
-    __device__ void init() {
+    uint32_t smax[4], smin[4];
+    __device__ __forceinline__ void init() {
 #pragma unroll
-        for (int q = 0; q < R; ++q) {
+        for (int q = 0; q < 4; ++q) {
+            smax[q] = DT::kPerVec == 8 ? 0x80008000u : 0x80000000u;
+            smin[q] = DT::kPerVec == 8 ? 0x7FFF7FFFu : 0x7FFFFFFFu;
+        }
+    }
+    __device__ __forceinline__ void add(const u32x4& v) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t w = word(v, q);
             if constexpr (DT::kPerVec == 8) {
-                smax[q] = 0x80008000u;  // two int16 minima
-                smin[q] = 0x7FFF7FFFu;
-                umax[q] = 0u;
+                smax[q] = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(as_s16x2_r(smax[q]), as_s16x2_r(w)));
+                smin[q] = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(as_s16x2_r(smin[q]), as_s16x2_r(w)));
             } else {
-                smax[q] = 0x80000000u;
-                smin[q] = 0x7FFFFFFFu;
-                umax[q] = 0u;
+                smax[q] = (uint32_t)max_i32((int)smax[q], (int)w);
+                smin[q] = (uint32_t)min_i32((int)smin[q], (int)w);
             }
         }
     }
-    __device__ void add(const u32x4& v) {
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int q = 0; q < R; ++q) {
-            if constexpr (DT::kPerVec == 8) {
-                smax[q] = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(as_s16x2_r(smax[q]), as_s16x2_r(w[q])));
-                smin[q] = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(as_s16x2_r(smin[q]), as_s16x2_r(w[q])));
-                umax[q] = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(as_u16x2_r(umax[q]), as_u16x2_r(w[q])));
-            } else {
-                smax[q] = (uint32_t)max_i32((int)smax[q], (int)w[q]);
-                smin[q] = (uint32_t)min_i32((int)smin[q], (int)w[q]);
-                umax[q] = max_u32(umax[q], w[q]);
-            }
-        }
-    }
-    // exact maximum order of column j
-    __device__ uint32_t order(int j) const {
+    __device__ __forceinline__ uint32_t order(int j) const {
         if constexpr (DT::kPerVec == 8) {
             const int q = j >> 1, sh = (j & 1) * 16;
             const int M = (int)(int16_t)(smax[q] >> sh);
             const int m = (int)(int16_t)(smin[q] >> sh);
-            const uint32_t U = (umax[q] >> sh) & 0xFFFFu;
-            if (U > 0xFF80u) return DT::kNanOrder;
             return M >= 0 ? DT::order((uint32_t)M) : DT::order((uint32_t)m & 0xFFFFu);
         } else {
-            if (umax[j] > 0xFF800000u) return DT::kNanOrder;
             return (int)smax[j] >= 0 ? DT::order(smax[j]) : DT::order(smin[j]);
         }
     }
 };
 
-// Exact path for one column of a segment whose buffer overflowed: one wave
-// re-reads the column's rows [r_lo, r_hi) (stride ld) at every step of an
-// exact bit search.  Writes the column's top-k (sorted) to out, returns n.
+// Sum of v over the TPC consecutive lanes of one column's thread group.
+template <int TPC>
+__device__ __forceinline__ uint32_t group_sum(uint32_t v) {
+#pragma unroll
+    for (int off = 1; off < TPC; off <<= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Exact path for one column of a segment: one wave re-reads the column's rows
+// [r_lo, r_hi) (stride ld) at every step of an exact bit search and writes
+// the column's top-k (sorted) to out; returns n.
 template <class DT>
 __device__ __noinline__ uint32_t exact_row_column(const typename DT::storage* x, int64_t ld, uint32_t col,
                                                   uint32_t r_lo, uint32_t r_hi, uint64_t* buf,
@@ -153,14 +251,120 @@ __device__ __noinline__ uint32_t exact_row_column(const typename DT::storage* x,
     return wave_exact_topk<DT::kOrderBits>(buf, cap, out, visit, k);
 }
 
-template <class DT, int NV>
+// Keeps the candidates of one column whose order is at least the k-th
+// largest order among the n of them (all of them when n <= k), compacted in
+// place.  Called by the column's TPC threads (consecutive lanes of one wave);
+// thread q holds candidates q, q + TPC, ...  Returns the new count and sets
+// T_out to that k-th largest order (0 when n <= k).
+template <class DT, int CAP>
+__device__ __forceinline__ uint32_t trim_column(uint64_t* cand, uint32_t q, uint32_t n, uint32_t k,
+                                                uint32_t* T_out) {
+    constexpr int TPC = RowTile<DT>::TPC;
+    constexpr int VPT = CAP / TPC;
+    constexpr int OB = DT::kOrderBits;
+    uint32_t o[VPT];
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const uint32_t idx = q + (uint32_t)v * TPC;
+        o[v] = idx < n ? key_order(cand[idx]) : 0u;
+    }
+    uint32_t T = 0;
+    if (n > k) {
+#pragma unroll 1
+        for (int b = OB - 1; b >= 0; --b) {
+            const uint32_t c = T | (1u << b);
+            uint32_t m = 0;
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) m += o[v] >= c ? 1u : 0u;
+            if (group_sum<TPC>(m) >= k) T = c;
+        }
+    }
+    *T_out = T;
+    // In-place stable compaction with the TPC threads in step: at step v
+    // every index below (v + 1) * TPC has been read, and a kept key moves to
+    // an index at or below its own.
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint64_t gmask = ((1ull << TPC) - 1ull) << (lane & ~(uint32_t)(TPC - 1));
+    const uint64_t below = (1ull << lane) - 1ull;
+    uint32_t out = 0;
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const uint32_t idx = q + (uint32_t)v * TPC;
+        const bool keep = idx < n && o[v] >= T;
+        const uint64_t bal = __ballot(keep) & gmask;
+        const uint64_t key = keep ? cand[idx] : 0ull;
+        if (keep) cand[out + (uint32_t)__popcll(bal & below)] = key;
+        out += (uint32_t)__popcll(bal);
+    }
+    return out;
+}
+
+// Rebuilds the buffer of a column that overflowed during the pass covering
+// rows [pass_lo, pass_hi): one wave takes the buffer's keys from earlier
+// passes (all of the column's elements there at or above its threshold) and
+// re-reads the pass's rows, finds the k-th largest order T among them, and
+// keeps every key at or above T.  Still more than CAP keys (massive ties)
+// flags the column for the exact path.
+template <class DT, int NV, int CAP>
+__device__ __noinline__ void rebuild_column(RowShared<DT, CAP>& sh, const typename DT::storage* x, int64_t ld,
+                                            uint32_t colx, uint32_t col, uint32_t pass_lo, uint32_t pass_hi,
+                                            uint32_t k) {
+    using F = RowFilter<DT>;
+    constexpr int PRE = (CAP + 63) / 64;             // buffer keys per lane
+    constexpr int PER = kRowsPerStep * NV / 64;      // pass rows per lane
+    constexpr int OB = DT::kOrderBits;
+    const uint32_t lane = threadIdx.x & 63u;
+    uint64_t key[PRE + PER];
+    bool valid[PRE + PER];
+#pragma unroll
+    for (int j = 0; j < PRE; ++j) {
+        const uint32_t idx = (uint32_t)j * 64u + lane;
+        key[j] = idx < (uint32_t)CAP ? sh.cand[colx][idx] : 0ull;
+        valid[j] = idx < (uint32_t)CAP && key_row(key[j]) < pass_lo;
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const uint32_t r = pass_lo + (uint32_t)j * 64u + lane;
+        valid[PRE + j] = r < pass_hi;
+        const uint32_t raw = r < pass_hi ? (uint32_t)x[(int64_t)r * ld + col] : 0u;
+        key[PRE + j] = make_key(DT::order(raw), r, 0u);
+    }
+    uint32_t T = 0;
+#pragma unroll 1
+    for (int b = OB - 1; b >= 0; --b) {
+        const uint32_t c = T | (1u << b);
+        uint32_t n = 0;
+#pragma unroll
+        for (int j = 0; j < PRE + PER; ++j) n += (uint32_t)__popcll(__ballot(valid[j] && key_order(key[j]) >= c));
+        if (n >= k) T = c;
+    }
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int j = 0; j < PRE + PER; ++j)
+        cnt = wave_append(sh.cand[colx], cnt, CAP, valid[j] && key_order(key[j]) >= T, key[j]);
+    if (lane == 0) {
+        sh.cnt[colx] = cnt;
+        if (cnt > (uint32_t)CAP) sh.flag[colx] |= 1u;
+        if (T > sh.thr[colx]) {
+            uint32_t fmv, fqv;
+            F::encode(T, fmv, fqv);
+            sh.thr[colx] = T;
+            sh.fm[colx] = (typename DT::storage)fmv;
+            sh.fq[colx] = (typename DT::storage)fqv;
+        }
+    }
+}
+
+template <class DT, int NV, int CAP>
 __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
     using storage = typename DT::storage;
-    constexpr int TW = RowShape<DT>::kCols;
-    constexpr int CPV = DT::kPerVec;
+    using F = RowFilter<DT>;
+    constexpr int TW = RowTile<DT>::TW;
+    constexpr int CPV = RowTile<DT>::CPV;
+    constexpr int TPC = RowTile<DT>::TPC;
     constexpr int OB = DT::kOrderBits;
     static_assert(NV % 2 == 0, "two row groups per pass");
-    __shared__ RowShared<DT> sh;
+    __shared__ RowShared<DT, CAP> sh;
 
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
     const uint32_t k = (uint32_t)a.k;
@@ -173,23 +377,26 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
     const uint32_t r_lo = (uint32_t)((uint64_t)V * s / S), r_hi = (uint32_t)((uint64_t)V * (s + 1) / S);
     const storage* x = static_cast<const storage*>(a.x);
 
-    const uint32_t rsub = tid / kRowLanesPerRow;          // row within a 32-row step
-    const uint32_t g = tid % kRowLanesPerRow;             // 16-byte group within the tile
-    const uint32_t cg = c0 + g * CPV;                     // first column of this lane
-    const uint32_t ncols = cg < C ? min_u32((uint32_t)CPV, C - cg) : 0u;  // valid columns of this lane
+    const uint32_t rsub = tid / kRowLanesPerRow;     // row within a 32-row step
+    const uint32_t g = tid % kRowLanesPerRow;        // 16-byte group within the tile
+    const uint32_t cg = c0 + g * CPV;                // first column of this lane
+    const uint32_t ncols = cg < C ? min_u32((uint32_t)CPV, C - cg) : 0u;
     const bool vec_ok = a.vec_loads != 0 && ncols == (uint32_t)CPV;
 
-    for (uint32_t t = tid; t < (uint32_t)TW; t += kBlock) {
-        sh.thr[t] = 0;
-        sh.cnt[t] = 0;
+    // column-parallel steps: TPC consecutive threads per tile column
+    const uint32_t pcol = tid / TPC, pq = tid % TPC;
+
+    if (tid < (uint32_t)TW) {
+        sh.thr[tid] = 0;
+        sh.cnt[tid] = 0;
+        sh.flag[tid] = 0;
     }
-    __syncthreads();
 
     const uint32_t per_pass = (uint32_t)kRowsPerStep * NV;
     const uint32_t npass = r_hi > r_lo ? (r_hi - r_lo + per_pass - 1) / per_pass : 0u;
-    for (uint32_t p = 0; p < npass; ++p) {
+
+    auto load_pass = [&](u32x4(&d)[NV], uint32_t p) {
         const uint32_t rbase = r_lo + p * per_pass + rsub;
-        u32x4 d[NV];
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const uint32_t r = rbase + (uint32_t)i * kRowsPerStep;
@@ -197,8 +404,8 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
             if (r < r_hi && vec_ok) {
                 d[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
             } else {
-                // partial vector (row past the segment, columns past C, or an
-                // unaligned layout): element loads, -Inf where nothing is read
+                // a partial vector (row past the segment, columns past C, or
+                // rows not 16-byte aligned): element loads, -Inf elsewhere
                 uint32_t e[CPV];
 #pragma unroll
                 for (int j = 0; j < CPV; ++j)
@@ -209,91 +416,223 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
                     d[i] = u32x4{e[0], e[1], e[2], e[3]};
             }
         }
+    };
 
-        // (1) two representatives per column: even and odd row-steps
-        ColMax<DT> m0, m1;
-        m0.init();
-        m1.init();
+    // Turn the wave's queued row vectors into candidate keys, one vector per
+    // lane (wave-uniform qcnt).
+    auto flush = [&](uint32_t qcnt) {
+        for (uint32_t b = 0; b < qcnt; b += 64u) {
+            const uint32_t e = b + lane;
+            if (e < qcnt) {
+                const u32x4 d = sh.qdata[wave][e];
+                const uint32_t meta = sh.qmeta[wave][e];
+                const uint32_t row = meta >> 3, gg = meta & 7u;
+                const uint32_t nc = min_u32((uint32_t)CPV, C - (c0 + gg * CPV));  // queued lanes have columns < C
+                const u32x4 fmw = *reinterpret_cast<const u32x4*>(&sh.fm[gg * CPV]);
+                const u32x4 fqw = *reinterpret_cast<const u32x4*>(&sh.fq[gg * CPV]);
+                uint32_t mask = 0;
 #pragma unroll
-        for (int i = 0; i < NV; i += 2) {
-            m0.add(d[i]);
-            m1.add(d[i + 1]);
-        }
-        uint32_t lane_max[CPV];
-#pragma unroll
-        for (int j = 0; j < CPV; ++j) {
-            const uint32_t o0 = m0.order(j), o1 = m1.order(j);
-            lane_max[j] = max_u32(o0, o1);
-            sh.reps[g * CPV + j][rsub * 2] = o0;
-            sh.reps[g * CPV + j][rsub * 2 + 1] = o1;
-        }
-        __syncthreads();
-
-        // (2) k-th largest of each column's 64 representatives; 4 threads per
-        //     column, 16 representatives each, sums over the 4 with shuffles
-        for (uint32_t col = tid / 4; col < (uint32_t)TW; col += kBlock / 4) {
-            const uint32_t q = tid & 3u;
-            uint32_t v[16];
-#pragma unroll
-            for (int j = 0; j < 16; ++j) v[j] = sh.reps[col][q * 16 + j];
-            uint32_t t = 0;
-#pragma unroll 1
-            for (int b = OB - 1; b >= 0; --b) {
-                const uint32_t cand = t | (1u << b);
-                uint32_t n = 0;
-#pragma unroll
-                for (int j = 0; j < 16; ++j) n += v[j] >= cand ? 1u : 0u;
-                n += __shfl_xor(n, 1, 64);
-                n += __shfl_xor(n, 2, 64);
-                if (n >= k) t = cand;
-            }
-            if (q == 0 && t > sh.thr[col]) sh.thr[col] = t;
-        }
-        __syncthreads();
-
-        // (3) append the elements at or above each column's threshold
-        uint32_t thr[CPV];
-#pragma unroll
-        for (int j = 0; j < CPV; ++j) thr[j] = sh.thr[(g * CPV + j) % TW];
-#pragma unroll
-        for (int j = 0; j < CPV; ++j) {
-            if ((uint32_t)j < ncols && lane_max[j] >= thr[j]) {
-                const uint32_t colx = g * CPV + j;
-#pragma unroll
-                for (int i = 0; i < NV; ++i) {
-                    const uint32_t r = rbase + (uint32_t)i * kRowsPerStep;
-                    const uint32_t o = DT::order(row_elem<DT>(d[i], j));
-                    if (r < r_hi && o >= thr[j]) {
-                        const uint32_t pos = atomicAdd(&sh.cnt[colx], 1u);
-                        if (pos < (uint32_t)kRowCap) sh.cand[colx][pos] = make_key(o, r, 0u);
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t t = F::test(word(d, q), word(fmw, q), word(fqw, q));
+                    if constexpr (CPV == 8) {
+                        mask |= (F::passes(t, 0) ? 1u : 0u) << (2 * q);
+                        mask |= (F::passes(t, 1) ? 1u : 0u) << (2 * q + 1);
+                    } else {
+                        mask |= (F::passes(t, 0) ? 1u : 0u) << q;
                     }
+                }
+                mask &= (1u << nc) - 1u;
+                while (mask) {
+                    const uint32_t j = (uint32_t)__builtin_ctz(mask);
+                    mask &= mask - 1u;
+                    const uint32_t col = gg * CPV + j;
+                    const uint32_t o = DT::order(row_elem<DT>(d, j));
+                    const uint32_t pos = atomicAdd(&sh.cnt[col], 1u);
+                    if (pos < (uint32_t)CAP) sh.cand[col][pos] = make_key(o, row, 0u);
                 }
             }
         }
-        __syncthreads();  // reps and thresholds are rewritten by the next pass
+    };
+
+    u32x4 cur[NV], nxt[NV];
+    if (npass > 0) load_pass(cur, 0);
+    uint32_t nanacc[4] = {0u, 0u, 0u, 0u};
+    __syncthreads();
+
+    for (uint32_t p = 0; p < npass; ++p) {
+        if (p + 1 < npass) load_pass(nxt, p + 1);
+
+        if (p == 0) {
+            // (1) starting thresholds from 64 group maxima per column
+            ColMax<DT> m0, m1;
+            m0.init();
+            m1.init();
+#pragma unroll
+            for (int i = 0; i < NV; i += 2) {
+                m0.add(cur[i]);
+                m1.add(cur[i + 1]);
+            }
+            if (npass > 1) {  // the second pass is already loaded: group maxima over both
+#pragma unroll
+                for (int i = 0; i < NV; i += 2) {
+                    m0.add(nxt[i]);
+                    m1.add(nxt[i + 1]);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < CPV; ++j) {
+                sh.reps[g * CPV + j][rsub * 2] = m0.order(j);
+                sh.reps[g * CPV + j][rsub * 2 + 1] = m1.order(j);
+            }
+            __syncthreads();
+            constexpr int RPT = kRowReps / TPC;
+            uint32_t v[RPT];
+#pragma unroll
+            for (int j = 0; j < RPT; ++j) v[j] = sh.reps[pcol][pq * RPT + j];
+            uint32_t T = 0;
+#pragma unroll 1
+            for (int b = OB - 1; b >= 0; --b) {
+                const uint32_t c = T | (1u << b);
+                uint32_t n = 0;
+#pragma unroll
+                for (int j = 0; j < RPT; ++j) n += v[j] >= c ? 1u : 0u;
+                if (group_sum<TPC>(n) >= k) T = c;
+            }
+            if (pq == 0) {
+                uint32_t fmv, fqv;
+                F::encode(T, fmv, fqv);
+                sh.thr[pcol] = T;
+                sh.fm[pcol] = (storage)fmv;
+                sh.fq[pcol] = (storage)fqv;
+            }
+            __syncthreads();
+        }
+
+        // (2) raw filter of every row vector; lanes with a passing element queue it
+        {
+            const u32x4 fmw = *reinterpret_cast<const u32x4*>(&sh.fm[g * CPV]);
+            const u32x4 fqw = *reinterpret_cast<const u32x4*>(&sh.fq[g * CPV]);
+            const uint32_t rbase = r_lo + p * per_pass + rsub;
+            uint32_t qcnt = 0;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const uint32_t r = rbase + (uint32_t)i * kRowsPerStep;
+                uint32_t any = 0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    any |= F::test(word(cur[i], q), word(fmw, q), word(fqw, q));
+                    nanacc[q] = F::umax(nanacc[q], word(cur[i], q));
+                }
+                const bool has = any != 0u && r < r_hi && ncols != 0u;
+                const unsigned long long bal = __ballot(has);
+                if (bal) {
+                    if (has) {
+                        const uint32_t pos = qcnt + lanes_below(bal);
+                        sh.qdata[wave][pos] = cur[i];
+                        sh.qmeta[wave][pos] = (r << 3) | g;
+                    }
+                    qcnt += (uint32_t)__popcll(bal);
+                    if (qcnt > (uint32_t)(kRowQueue - 64)) {
+                        flush(qcnt);
+                        qcnt = 0;
+                    }
+                }
+            }
+            flush(qcnt);
+        }
+        __syncthreads();
+
+        // (3) a column whose buffer overflowed in this pass is rebuilt from
+        //     this pass's rows; before another pass, a column holding more
+        //     than max(2k, 24) keys is trimmed to its running top-k
+        {
+            const uint32_t n = sh.cnt[pcol];
+            if (p + 1 < npass && n <= (uint32_t)CAP && n > max_u32(2u * k, 24u)) {
+                uint32_t T;
+                const uint32_t kept = trim_column<DT, CAP>(sh.cand[pcol], pq, n, k, &T);
+                if (pq == 0) {
+                    sh.cnt[pcol] = kept;
+                    if (T > sh.thr[pcol]) {
+                        uint32_t fmv, fqv;
+                        F::encode(T, fmv, fqv);
+                        sh.thr[pcol] = T;
+                        sh.fm[pcol] = (storage)fmv;
+                        sh.fq[pcol] = (storage)fqv;
+                    }
+                }
+            }
+            const uint32_t pass_lo = r_lo + p * per_pass;
+            const uint32_t pass_hi = min_u32(pass_lo + per_pass, r_hi);
+            for (uint32_t colx = wave; colx < (uint32_t)TW; colx += kWaves) {
+                if (c0 + colx >= C) break;
+                if (sh.cnt[colx] > (uint32_t)CAP && (sh.flag[colx] & 1u) == 0u)
+                    rebuild_column<DT, NV, CAP>(sh, x, a.ld, colx, c0 + colx, pass_lo, pass_hi, k);
+            }
+        }
+        if (p + 1 < npass) {
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < NV; ++i) cur[i] = nxt[i];
+        }
     }
 
-    // (4) per column: exact top-k of the candidates still at or above T_c
-    uint64_t* out_lists = a.partials;
+    // columns that hold a negative NaN take the exact path
+#pragma unroll
+    for (int j = 0; j < CPV; ++j)
+        if ((uint32_t)j < ncols && F::has_negative_nan(nanacc[j * 4 / CPV], j % (CPV / 4)))
+            atomicOr(&sh.flag[g * CPV + j], 2u);
+    __syncthreads();
+
+    // (4) the segment's top-k set of every column, unsorted
+    uint64_t* lists = a.partials;
+    {
+        const uint32_t col = c0 + pcol;
+        const uint32_t n = sh.cnt[pcol];
+        if (col < C && sh.flag[pcol] == 0u && n <= (uint32_t)CAP) {
+            uint64_t* cand = sh.cand[pcol];
+            uint32_t T;
+            uint32_t kept = trim_column<DT, CAP>(cand, pq, n, k, &T);
+            if (kept > k) {
+                // ties at the k-th order: search the row bits for the k-th largest key
+                constexpr int VPT = CAP / TPC;
+                uint64_t kk[VPT];
+#pragma unroll
+                for (int v = 0; v < VPT; ++v) {
+                    const uint32_t idx = pq + (uint32_t)v * TPC;
+                    kk[v] = idx < kept ? cand[idx] : 0ull;
+                }
+                uint64_t K = (uint64_t)T << 32;
+#pragma unroll 1
+                for (int b = 31; b >= 8; --b) {
+                    const uint64_t c = K | (1ull << b);
+                    uint32_t m = 0;
+#pragma unroll
+                    for (int v = 0; v < VPT; ++v) m += kk[v] >= c ? 1u : 0u;
+                    if (group_sum<TPC>(m) >= k) K = c;
+                }
+                const uint64_t gmask = ((1ull << TPC) - 1ull) << (lane & ~(uint32_t)(TPC - 1));
+                const uint64_t below = (1ull << lane) - 1ull;
+                uint32_t out = 0;
+#pragma unroll
+                for (int v = 0; v < VPT; ++v) {
+                    const bool keep = kk[v] >= K;
+                    const uint64_t bal = __ballot(keep) & gmask;
+                    if (keep) cand[out + (uint32_t)__popcll(bal & below)] = kk[v];
+                    out += (uint32_t)__popcll(bal);
+                }
+                kept = out;
+            }
+            uint64_t* dst = lists + ((int64_t)col * S + s) * k;
+            for (uint32_t t = pq; t < k; t += TPC) dst[t] = t < kept ? cand[t] : 0ull;
+        }
+    }
+    // flagged or overflowed columns: exact search over the segment, one wave per column
     for (uint32_t colx = wave; colx < (uint32_t)TW; colx += kWaves) {
         const uint32_t col = c0 + colx;
         if (col >= C) break;
-        uint64_t* dst = out_lists + ((int64_t)col * S + s) * k;
-        const uint32_t total = sh.cnt[colx];
-        uint32_t n;
-        if (total > (uint32_t)kRowCap) {
-            n = exact_row_column<DT>(x, a.ld, col, r_lo, r_hi, sh.cand[colx], kRowCap, sh.tmp[wave], k);
-        } else {
-            const uint64_t T = (uint64_t)sh.thr[colx] << 32;
-            uint32_t m = 0;
-            for (uint32_t b = 0; b < total; b += 64u) {
-                const uint32_t t = b + lane;
-                const uint64_t key = t < total ? sh.cand[colx][t] : 0ull;
-                // compact in place (reads of this round precede its writes)
-                m = wave_append(sh.cand[colx], m, kRowCap, t < total && key >= T, key);
-            }
-            n = wave_rank_select(sh.cand[colx], m, k, sh.tmp[wave]);
-        }
+        if (sh.flag[colx] == 0u && sh.cnt[colx] <= (uint32_t)CAP) continue;
+        const uint32_t n = exact_row_column<DT>(x, a.ld, col, r_lo, r_hi, sh.cand[colx], CAP, sh.tmp[wave], k);
+        uint64_t* dst = lists + ((int64_t)col * S + s) * k;
         if (lane < k) dst[lane] = lane < n ? sh.tmp[wave][lane] : 0ull;
     }
 }
@@ -303,7 +642,8 @@ template <class DT>
 __global__ __launch_bounds__(kBlock) void topk_row_merge(RowArgs a) {
     using storage = typename DT::storage;
     constexpr int OB = DT::kOrderBits;
-    __shared__ alignas(16) uint64_t buf[kWaves][kMaxK + 192];
+    constexpr int kBuf = kMaxK + 192;
+    __shared__ alignas(16) uint64_t buf[kWaves][kBuf];
     __shared__ alignas(16) uint64_t tmp[kWaves][kMaxK];
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
     const uint32_t col = blockIdx.x * kWaves + wave;
@@ -325,10 +665,10 @@ __global__ __launch_bounds__(kBlock) void topk_row_merge(RowArgs a) {
         for (int j = 0; j < kRowMergeKeysPerLane; ++j) f(keys[j], key_order(keys[j]) != 0);
     };
     uint32_t cnt = 0;
-    visit([&](uint64_t key, bool valid) { cnt = wave_append(buf[wave], cnt, kMaxK + 192, valid && key_order(key) >= T, key); });
+    visit([&](uint64_t key, bool valid) { cnt = wave_append(buf[wave], cnt, kBuf, valid && key_order(key) >= T, key); });
     uint32_t n;
-    if (cnt > (uint32_t)(kMaxK + 192))
-        n = wave_exact_topk<OB>(buf[wave], kMaxK + 192, tmp[wave], visit, k);
+    if (cnt > (uint32_t)kBuf)
+        n = wave_exact_topk<OB>(buf[wave], kBuf, tmp[wave], visit, k);
     else
         n = wave_rank_select(buf[wave], cnt, k, tmp[wave]);
     if (lane < k && lane < n) {
@@ -342,25 +682,30 @@ __global__ __launch_bounds__(kBlock) void topk_row_merge(RowArgs a) {
     }
 }
 
-template <class DT>
-hipError_t launch_row_dt(int nv, const RowArgs& a, hipStream_t stream) {
+template <class DT, int CAP>
+hipError_t launch_scan(int nv, const RowArgs& a, hipStream_t stream) {
     const dim3 grid((uint32_t)((int64_t)a.tiles * a.S)), block(kBlock);
     switch (nv) {
-        case 2: hipLaunchKernelGGL((topk_row_scan<DT, 2>), grid, block, 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((topk_row_scan<DT, 4>), grid, block, 0, stream, a); break;
-        case 8: hipLaunchKernelGGL((topk_row_scan<DT, 8>), grid, block, 0, stream, a); break;
+        case 8: hipLaunchKernelGGL((topk_row_scan<DT, 8, CAP>), grid, block, 0, stream, a); break;
+        case 16: hipLaunchKernelGGL((topk_row_scan<DT, 16, CAP>), grid, block, 0, stream, a); break;
         default: return hipErrorInvalidValue;
     }
-    hipError_t e = hipGetLastError();
+    return hipGetLastError();
+}
+
+template <class DT>
+hipError_t launch_row_dt(int nv, const RowArgs& a, hipStream_t stream) {
+    const hipError_t e = a.k <= kRowSmallK ? launch_scan<DT, kRowCapSmall>(nv, a, stream)
+                                           : launch_scan<DT, kRowCapLarge>(nv, a, stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((topk_row_merge<DT>), dim3((uint32_t)((a.C + kWaves - 1) / kWaves)), block, 0,
+    hipLaunchKernelGGL((topk_row_merge<DT>), dim3((uint32_t)((a.C + kWaves - 1) / kWaves)), dim3(kBlock), 0,
                        stream, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-int row_tile_columns(int dtype) { return dtype == 0 ? RowShape<Bf16>::kCols : RowShape<F32>::kCols; }
+int row_tile_columns(int dtype) { return dtype == 0 ? RowTile<Bf16>::TW : RowTile<F32>::TW; }
 
 hipError_t launch_row(int dtype, int nv, const RowArgs& a, hipStream_t stream) {
     return dtype == 0 ? launch_row_dt<Bf16>(nv, a, stream) : launch_row_dt<F32>(nv, a, stream);
