@@ -140,12 +140,6 @@ __device__ __forceinline__ uint32_t wave_kth_largest(uint32_t v, uint32_t k) {
     return t;
 }
 
-__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
-
 // Number of lanes below this one whose bit is set in `mask`.
 __device__ __forceinline__ uint32_t lanes_below(unsigned long long mask) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
@@ -212,16 +206,16 @@ __device__ __forceinline__ uint32_t wave_rank_select(const uint64_t* keys, uint3
 template <int OrderBits, class Visit>
 __device__ __forceinline__ uint32_t wave_exact_topk(uint64_t* buf, uint32_t cap, uint64_t* out,
                                                     const Visit& visit, uint32_t k) {
-    uint32_t local = 0;
-    visit([&](uint64_t, bool valid) { local += valid ? 1u : 0u; });
-    const uint32_t total = wave_sum(local);
+    // counts are wave-wide: one ballot per key slot (visit is wave-uniform)
+    uint32_t total = 0;
+    visit([&](uint64_t, bool valid) { total += (uint32_t)__popcll(__ballot(valid)); });
     uint64_t thr = 0;
     if (total > k) {
         for (int b = 32 + OrderBits - 1; b >= 8; --b) {
             const uint64_t cand = thr | (1ull << b);
             uint32_t n = 0;
-            visit([&](uint64_t key, bool valid) { n += (valid && key >= cand) ? 1u : 0u; });
-            if (wave_sum(n) >= k) thr = cand;
+            visit([&](uint64_t key, bool valid) { n += (uint32_t)__popcll(__ballot(valid && key >= cand)); });
+            if (n >= k) thr = cand;
         }
     }
     uint32_t cnt = 0;

@@ -32,9 +32,9 @@
 //     candidates, which becomes the new T_c, and compact the buffer in place.
 //     T_c then follows the segment's own k-th largest, so later passes add
 //     few candidates.
-//  4. At the end the same trim runs on every column, and a search over the
-//     row bits breaks ties at the k-th order: exactly k keys remain, written
-//     unsorted to the segment's slot of the partial lists.
+//  4. At the end a rank count over each column's candidates (trimmed first
+//     if many) writes the column's top k, sorted, to the segment's slot of
+//     the partial lists.
 // A column whose buffer overflows during a pass is rebuilt at the end of the
 // pass: one wave re-reads the pass's rows of that column and keeps what is at
 // or above the exact k-th largest order seen so far.  Negative NaNs never
@@ -42,9 +42,10 @@
 // a column, like one that still overflows after a rebuild (massive ties), is
 // re-read over the whole segment by one wave and selected by an exact search.
 //
-// Merge kernel: one wave per column selects the top k of its S partial lists
-// (the k-th largest of the lanes' maxima as threshold, then a rank count) and
-// writes the output.  The kernel boundary orders it after the scan.
+// Merge kernel: one wave per column selects the top k of its S sorted
+// partial lists (each lane holds a contiguous run of them; the k-th largest
+// of the lanes' maxima is the threshold, then a rank count) and writes the
+// output.  The kernel boundary orders it after the scan.
 #include "topk_device.hpp"
 #include "topk_internal.hpp"
 
@@ -223,12 +224,62 @@ struct ColMax {
     }
 };
 
-// Sum of v over the TPC consecutive lanes of one column's thread group.
+// Value of v in a partner lane through a DPP lane permutation (no LDS
+// round trip): 0xB1 swaps neighbours within a quad, 0x4E swaps the two lane
+// pairs of a quad, 0x141 mirrors each half-row of 8 lanes.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Sum, maximum and minimum of v over the TPC (4 or 8) consecutive lanes of
+// one column's thread group, all of them active.
 template <int TPC>
 __device__ __forceinline__ uint32_t group_sum(uint32_t v) {
-#pragma unroll
-    for (int off = 1; off < TPC; off <<= 1) v += __shfl_xor(v, off, 64);
+    static_assert(TPC == 4 || TPC == 8, "quads or half-rows");
+    v += dpp_mov<0xB1>(v);
+    v += dpp_mov<0x4E>(v);
+    if constexpr (TPC == 8) v += dpp_mov<0x141>(v);
     return v;
+}
+template <int TPC>
+__device__ __forceinline__ uint32_t group_max(uint32_t v) {
+    v = max_u32(v, dpp_mov<0xB1>(v));
+    v = max_u32(v, dpp_mov<0x4E>(v));
+    if constexpr (TPC == 8) v = max_u32(v, dpp_mov<0x141>(v));
+    return v;
+}
+template <int TPC>
+__device__ __forceinline__ uint32_t group_min(uint32_t v) {
+    v = min_u32(v, dpp_mov<0xB1>(v));
+    v = min_u32(v, dpp_mov<0x4E>(v));
+    if constexpr (TPC == 8) v = min_u32(v, dpp_mov<0x141>(v));
+    return v;
+}
+
+// The k-th largest of the values a thread group holds (VPT per thread, empty
+// slots 0), by bisection of [lo, hi] where at least k values are >= lo and
+// hi is the largest value: about log2(hi - lo) counting rounds.
+template <int TPC, int VPT>
+__device__ __forceinline__ uint32_t group_kth(const uint32_t (&v)[VPT], uint32_t k, uint32_t lo, uint32_t hi) {
+    while (lo < hi) {
+        const uint32_t mid = lo + (hi - lo + 1u) / 2u;
+        uint32_t m = 0;
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) m += v[j] >= mid ? 1u : 0u;
+        if (group_sum<TPC>(m) >= k) lo = mid;
+        else hi = mid - 1u;
+    }
+    return lo;
+}
+
+// Bit i set for each column i < TW of the tile taken by wave w (columns w,
+// w + kWaves, ...) that satisfies pred(column); wave-uniform.
+template <int TW, class Pred>
+__device__ __forceinline__ uint64_t wave_columns(uint32_t w, const Pred& pred) {
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t colx = w + lane * kWaves;
+    return __ballot(colx < (uint32_t)TW && pred(colx));
 }
 
 // Exact path for one column of a segment: one wave re-reads the column's rows
@@ -253,32 +304,25 @@ __device__ __noinline__ uint32_t exact_row_column(const typename DT::storage* x,
 
 // Keeps the candidates of one column whose order is at least the k-th
 // largest order among the n of them (all of them when n <= k), compacted in
-// place.  Called by the column's TPC threads (consecutive lanes of one wave);
-// thread q holds candidates q, q + TPC, ...  Returns the new count and sets
-// T_out to that k-th largest order (0 when n <= k).
+// place.  Every candidate's order is at least thr.  Called by the column's
+// TPC threads (consecutive lanes of one wave); thread q holds candidates q,
+// q + TPC, ...  Returns the new count and sets T_out to that k-th largest
+// order (thr when n <= k).
 template <class DT, int CAP>
-__device__ __forceinline__ uint32_t trim_column(uint64_t* cand, uint32_t q, uint32_t n, uint32_t k,
+__device__ __forceinline__ uint32_t trim_column(uint64_t* cand, uint32_t q, uint32_t n, uint32_t k, uint32_t thr,
                                                 uint32_t* T_out) {
     constexpr int TPC = RowTile<DT>::TPC;
     constexpr int VPT = CAP / TPC;
-    constexpr int OB = DT::kOrderBits;
     uint32_t o[VPT];
+    uint32_t mx = 0;
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
         const uint32_t idx = q + (uint32_t)v * TPC;
         o[v] = idx < n ? key_order(cand[idx]) : 0u;
+        mx = max_u32(mx, o[v]);
     }
-    uint32_t T = 0;
-    if (n > k) {
-#pragma unroll 1
-        for (int b = OB - 1; b >= 0; --b) {
-            const uint32_t c = T | (1u << b);
-            uint32_t m = 0;
-#pragma unroll
-            for (int v = 0; v < VPT; ++v) m += o[v] >= c ? 1u : 0u;
-            if (group_sum<TPC>(m) >= k) T = c;
-        }
-    }
+    uint32_t T = thr;
+    if (n > k) T = group_kth<TPC, VPT>(o, k, thr, group_max<TPC>(mx));
     *T_out = T;
     // In-place stable compaction with the TPC threads in step: at step v
     // every index below (v + 1) * TPC has been read, and a kept key moves to
@@ -299,12 +343,6 @@ __device__ __forceinline__ uint32_t trim_column(uint64_t* cand, uint32_t q, uint
     return out;
 }
 
-// Rebuilds the buffer of a column that overflowed during the pass covering
-// rows [pass_lo, pass_hi): one wave takes the buffer's keys from earlier
-// passes (all of the column's elements there at or above its threshold) and
-// re-reads the pass's rows, finds the k-th largest order T among them, and
-// keeps every key at or above T.  Still more than CAP keys (massive ties)
-// flags the column for the exact path.
 template <class DT, int NV, int CAP>
 __device__ __noinline__ void rebuild_column(RowShared<DT, CAP>& sh, const typename DT::storage* x, int64_t ld,
                                             uint32_t colx, uint32_t col, uint32_t pass_lo, uint32_t pass_hi,
@@ -489,15 +527,14 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
             uint32_t v[RPT];
 #pragma unroll
             for (int j = 0; j < RPT; ++j) v[j] = sh.reps[pcol][pq * RPT + j];
-            uint32_t T = 0;
-#pragma unroll 1
-            for (int b = OB - 1; b >= 0; --b) {
-                const uint32_t c = T | (1u << b);
-                uint32_t n = 0;
+            uint32_t vmin = v[0], vmax = v[0];
 #pragma unroll
-                for (int j = 0; j < RPT; ++j) n += v[j] >= c ? 1u : 0u;
-                if (group_sum<TPC>(n) >= k) T = c;
+            for (int j = 1; j < RPT; ++j) {
+                vmin = min_u32(vmin, v[j]);
+                vmax = max_u32(vmax, v[j]);
             }
+            // all 64 are >= the minimum, and k <= 64
+            const uint32_t T = group_kth<TPC, RPT>(v, k, group_min<TPC>(vmin), group_max<TPC>(vmax));
             if (pq == 0) {
                 uint32_t fmv, fqv;
                 F::encode(T, fmv, fqv);
@@ -549,7 +586,7 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
             const uint32_t n = sh.cnt[pcol];
             if (p + 1 < npass && n <= (uint32_t)CAP && n > max_u32(2u * k, 24u)) {
                 uint32_t T;
-                const uint32_t kept = trim_column<DT, CAP>(sh.cand[pcol], pq, n, k, &T);
+                const uint32_t kept = trim_column<DT, CAP>(sh.cand[pcol], pq, n, k, sh.thr[pcol], &T);
                 if (pq == 0) {
                     sh.cnt[pcol] = kept;
                     if (T > sh.thr[pcol]) {
@@ -563,10 +600,13 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
             }
             const uint32_t pass_lo = r_lo + p * per_pass;
             const uint32_t pass_hi = min_u32(pass_lo + per_pass, r_hi);
-            for (uint32_t colx = wave; colx < (uint32_t)TW; colx += kWaves) {
-                if (c0 + colx >= C) break;
-                if (sh.cnt[colx] > (uint32_t)CAP && (sh.flag[colx] & 1u) == 0u)
-                    rebuild_column<DT, NV, CAP>(sh, x, a.ld, colx, c0 + colx, pass_lo, pass_hi, k);
+            uint64_t todo = wave_columns<TW>(wave, [&](uint32_t colx) {
+                return c0 + colx < C && sh.cnt[colx] > (uint32_t)CAP && (sh.flag[colx] & 1u) == 0u;
+            });
+            while (todo) {
+                const uint32_t colx = wave + (uint32_t)__builtin_ctzll(todo) * kWaves;
+                todo &= todo - 1ull;
+                rebuild_column<DT, NV, CAP>(sh, x, a.ld, colx, c0 + colx, pass_lo, pass_hi, k);
             }
         }
         if (p + 1 < npass) {
@@ -583,54 +623,32 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
             atomicOr(&sh.flag[g * CPV + j], 2u);
     __syncthreads();
 
-    // (4) the segment's top-k set of every column, unsorted
+    // (4) the segment's top-k of every column, sorted
     uint64_t* lists = a.partials;
     {
         const uint32_t col = c0 + pcol;
         const uint32_t n = sh.cnt[pcol];
         if (col < C && sh.flag[pcol] == 0u && n <= (uint32_t)CAP) {
             uint64_t* cand = sh.cand[pcol];
-            uint32_t T;
-            uint32_t kept = trim_column<DT, CAP>(cand, pq, n, k, &T);
-            if (kept > k) {
-                // ties at the k-th order: search the row bits for the k-th largest key
-                constexpr int VPT = CAP / TPC;
-                uint64_t kk[VPT];
-#pragma unroll
-                for (int v = 0; v < VPT; ++v) {
-                    const uint32_t idx = pq + (uint32_t)v * TPC;
-                    kk[v] = idx < kept ? cand[idx] : 0ull;
-                }
-                uint64_t K = (uint64_t)T << 32;
-#pragma unroll 1
-                for (int b = 31; b >= 8; --b) {
-                    const uint64_t c = K | (1ull << b);
-                    uint32_t m = 0;
-#pragma unroll
-                    for (int v = 0; v < VPT; ++v) m += kk[v] >= c ? 1u : 0u;
-                    if (group_sum<TPC>(m) >= k) K = c;
-                }
-                const uint64_t gmask = ((1ull << TPC) - 1ull) << (lane & ~(uint32_t)(TPC - 1));
-                const uint64_t below = (1ull << lane) - 1ull;
-                uint32_t out = 0;
-#pragma unroll
-                for (int v = 0; v < VPT; ++v) {
-                    const bool keep = kk[v] >= K;
-                    const uint64_t bal = __ballot(keep) & gmask;
-                    if (keep) cand[out + (uint32_t)__popcll(bal & below)] = kk[v];
-                    out += (uint32_t)__popcll(bal);
-                }
-                kept = out;
+            uint32_t kept = n;
+            if (n > max_u32(2u * k, 32u)) {  // many left: trim to k plus ties first
+                uint32_t T;
+                kept = trim_column<DT, CAP>(cand, pq, n, k, sh.thr[pcol], &T);
             }
+            // rank what is left and write the top k, sorted, to the segment's list
             uint64_t* dst = lists + ((int64_t)col * S + s) * k;
-            for (uint32_t t = pq; t < k; t += TPC) dst[t] = t < kept ? cand[t] : 0ull;
+            rank_select(cand, kept, k, dst, pq, TPC);
+            for (uint32_t t = kept + pq; t < k; t += TPC) dst[t] = 0ull;
         }
     }
     // flagged or overflowed columns: exact search over the segment, one wave per column
-    for (uint32_t colx = wave; colx < (uint32_t)TW; colx += kWaves) {
+    uint64_t todo = wave_columns<TW>(wave, [&](uint32_t colx) {
+        return c0 + colx < C && (sh.flag[colx] != 0u || sh.cnt[colx] > (uint32_t)CAP);
+    });
+    while (todo) {
+        const uint32_t colx = wave + (uint32_t)__builtin_ctzll(todo) * kWaves;
+        todo &= todo - 1ull;
         const uint32_t col = c0 + colx;
-        if (col >= C) break;
-        if (sh.flag[colx] == 0u && sh.cnt[colx] <= (uint32_t)CAP) continue;
         const uint32_t n = exact_row_column<DT>(x, a.ld, col, r_lo, r_hi, sh.cand[colx], CAP, sh.tmp[wave], k);
         uint64_t* dst = lists + ((int64_t)col * S + s) * k;
         if (lane < k) dst[lane] = lane < n ? sh.tmp[wave][lane] : 0ull;
@@ -650,10 +668,13 @@ __global__ __launch_bounds__(kBlock) void topk_row_merge(RowArgs a) {
     if (col >= (uint32_t)a.C) return;
     const uint32_t k = (uint32_t)a.k, S = (uint32_t)a.S, M = S * k;
     const uint64_t* src = a.partials + (int64_t)col * M;
+    // Each lane takes a contiguous run of the sorted segment lists, so a
+    // lane's maximum is a segment maximum (k <= 16) and the k-th largest lane
+    // maximum is a tight threshold.
     uint64_t keys[kRowMergeKeysPerLane];
 #pragma unroll
     for (int j = 0; j < kRowMergeKeysPerLane; ++j) {
-        const uint32_t idx = (uint32_t)j * 64u + lane;
+        const uint32_t idx = lane * kRowMergeKeysPerLane + (uint32_t)j;
         keys[j] = idx < M ? src[idx] : 0ull;
     }
     uint64_t rep = 0;
