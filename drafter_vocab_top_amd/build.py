@@ -14,8 +14,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libtopk_cols.so")
-SOURCES = [os.path.join(CSRC, n) for n in ("topk_col.hip", "topk_row.hip", "topk_cols_api.cpp")]
-HEADERS = [os.path.join(CSRC, n) for n in ("topk_device.hpp", "topk_internal.hpp")] + \
+SOURCES = [os.path.join(CSRC, n) for n in ("topk_col.hip", "topk_colw.hip", "topk_row.hip", "topk_cols_api.cpp")]
+HEADERS = [os.path.join(CSRC, n) for n in ("topk_device.hpp", "topk_col_common.hpp", "topk_internal.hpp")] + \
           [os.path.join(INCLUDE, "topk_cols.h")]
 ARCH = "gfx950"
 

@@ -20,14 +20,17 @@
 //     never converted floats.  The signed maximum of raw patterns is the
 //     largest non-negative value; when a lane holds only negative patterns,
 //     the signed minimum is its largest value.
-//  3. Each wave, on its own, finds T, the k-th largest of its lanes' maxima,
-//     with a ballot bit-search.  k lanes hold an element at or above T, so
-//     no element below T can be in the wave's top-k, let alone the segment's.
-//  4. The wave's elements at or above T (usually about k of them) are found
-//     with a per-vector prefilter and an integer interval test on the raw
-//     pattern.  Ballot/mbcnt compaction collects them as 64-bit keys in the
-//     wave's LDS area.  The wave then copies them after the carried best
-//     keys in the workgroup area (one LDS atomic per wave).
+//  3. Each wave finds the k-th largest of its lanes' maxima with a ballot
+//     bit-search: k lanes hold an element at or above it, so it bounds the
+//     wave's, and the workgroup's, k-th largest element from below.  The
+//     largest of the four waves' bounds is the workgroup's threshold T.
+//  4. The elements at or above T (usually about k of them) are found with a
+//     per-vector prefilter and an integer interval test on the raw pattern.
+//     With two vectors per lane they are tested in place; with more, the
+//     vectors that reach T are queued in LDS and drained one vector per lane.
+//     Ballot/mbcnt compaction collects the passing elements as 64-bit keys
+//     in the wave's LDS area; the wave then copies them after the carried
+//     best keys in the workgroup area (one LDS atomic per wave).
 //  5. After one workgroup barrier, a rank count over that area gives the
 //     segment's exact top-k.  A segment that needs several passes carries it
 //     into the next pass as a running threshold.
@@ -44,6 +47,7 @@
 // store lands.  All four of its waves then select from the S*k keys: per-wave
 // thresholds, one barrier, one rank count.  It writes the output and resets
 // the ticket for the next run.
+#include "topk_col_common.hpp"
 #include "topk_device.hpp"
 #include "topk_internal.hpp"
 
@@ -57,106 +61,20 @@ constexpr int kWaveCap = 192;                // candidate slots per wave
 constexpr int kBlockCap = 512;               // carried best + candidates per workgroup
 constexpr int kMergeKeysPerThread = 16;      // S*k <= 4096 published keys, 16 per thread
 constexpr int kSpinLimit = 1 << 16;          // about 0.1 s: a store that has not landed by then never will
+constexpr int kQueue = 128;                  // queued vectors per wave
 
 struct ColShared {
     alignas(16) uint64_t cand[kBlockCap];          // [0, nbest) carried best, then candidates
     alignas(16) uint64_t best[kMaxK];              // rank-selection output, sorted
     alignas(16) uint64_t wbuf[kWaves][kWaveCap];   // each wave's candidates
     alignas(16) uint64_t wtmp[kWaves][kMaxK];      // each wave's exact-path result
+    alignas(16) u32x4 qdata[kWaves][kQueue];       // each wave's queued vectors
+    uint32_t qvec[kWaves][kQueue];                 // their vector indices
     uint32_t wave_thr[kWaves];
     uint32_t ncand;
     uint32_t overflow;
     uint32_t is_last;
 };
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ u32x4 load_vec(const u32x4* p) { return __builtin_nontemporal_load(p); }
-
-// Raw pattern of element e (0 <= e < kPerVec, known at compile time).
-template <class DT>
-__device__ __forceinline__ uint32_t vec_elem(const u32x4& v, int e) {
-    const uint32_t w = e < DT::kPerVec / 4 ? v.x
-                     : e < 2 * DT::kPerVec / 4 ? v.y
-                     : e < 3 * DT::kPerVec / 4 ? v.z : v.w;
-    if constexpr (DT::kPerVec == 8) return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
-    else return w;
-}
-
-// Raw pattern of element e, e known only at run time.
-template <class DT>
-__device__ __forceinline__ uint32_t vec_elem_dyn(const u32x4& v, uint32_t e) {
-    const uint32_t q = DT::kPerVec == 8 ? e >> 1 : e;
-    const uint32_t wx = v.x, wy = v.y, wz = v.z, ww = v.w;
-    const uint32_t w = q == 0 ? wx : q == 1 ? wy : q == 2 ? wz : ww;
-    if constexpr (DT::kPerVec == 8) return (w >> ((e & 1u) * 16u)) & 0xFFFFu;
-    else return w;
-}
-
-__device__ __forceinline__ s16x2 as_s16x2(uint32_t w) { return __builtin_bit_cast(s16x2, w); }
-__device__ __forceinline__ u16x2 as_u16x2(uint32_t w) { return __builtin_bit_cast(u16x2, w); }
-
-// Lane statistics of one pass (step 2).
-//   vmax[i]: raw signed maximum of vector i (bf16: two 16-bit halves packed)
-//   rep:     exact maximum order over the lane's elements, unless the lane
-//            holds a negative NaN (then neg_nan is set and rep is unused)
-// Invalid vector slots hold -Inf patterns, which never raise a maximum.
-template <class DT, int NV>
-__device__ __forceinline__ void lane_stats(const u32x4 (&d)[NV], uint32_t (&vmax)[NV],
-                                           uint32_t& rep, bool& neg_nan) {
-    if constexpr (DT::kPerVec == 8) {
-        s16x2 smax = {-32768, -32768}, smin = {32767, 32767};
-        u16x2 umax = {0, 0};
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            // Components go through scalars first: bit-casting a vector
-            // component (d[i].y) directly reads the vector's first element.
-            const uint32_t wx = d[i].x, wy = d[i].y, wz = d[i].z, ww = d[i].w;
-            const s16x2 a = as_s16x2(wx), b = as_s16x2(wy), c = as_s16x2(wz), e = as_s16x2(ww);
-            const s16x2 mx = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
-                                                       __builtin_elementwise_max(c, e));
-            const s16x2 mn = __builtin_elementwise_min(__builtin_elementwise_min(a, b),
-                                                       __builtin_elementwise_min(c, e));
-            const u16x2 ux = __builtin_elementwise_max(
-                __builtin_elementwise_max(as_u16x2(wx), as_u16x2(wy)),
-                __builtin_elementwise_max(as_u16x2(wz), as_u16x2(ww)));
-            vmax[i] = __builtin_bit_cast(uint32_t, mx);
-            smax = __builtin_elementwise_max(smax, mx);
-            smin = __builtin_elementwise_min(smin, mn);
-            umax = __builtin_elementwise_max(umax, ux);
-        }
-        const int M = max_i32((int)smax.x, (int)smax.y);
-        const int m = min_i32((int)smin.x, (int)smin.y);
-        rep = M >= 0 ? order_bf16((uint32_t)M) : order_bf16((uint32_t)m & 0xFFFFu);
-        neg_nan = max_u32((uint32_t)umax.x, (uint32_t)umax.y) > 0xFF80u;
-    } else {
-        int smax = INT32_MIN, smin = INT32_MAX;
-        uint32_t umax = 0;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const uint32_t wx = d[i].x, wy = d[i].y, wz = d[i].z, ww = d[i].w;
-            const int a = (int)wx, b = (int)wy, c = (int)wz, e = (int)ww;
-            const int mx = max_i32(max_i32(a, b), max_i32(c, e));
-            vmax[i] = (uint32_t)mx;
-            smax = max_i32(smax, mx);
-            smin = min_i32(smin, min_i32(min_i32(a, b), min_i32(c, e)));
-            umax = max_u32(umax, max_u32(max_u32(wx, wy), max_u32(wz, ww)));
-        }
-        rep = smax >= 0 ? order_f32((uint32_t)smax) : order_f32((uint32_t)smin);
-        neg_nan = umax > 0xFF800000u;
-    }
-}
-
-// Signed maximum held in a vmax entry.
-template <class DT>
-__device__ __forceinline__ int vec_max_signed(uint32_t vm) {
-    if constexpr (DT::kPerVec == 8) {
-        const s16x2 h = as_s16x2(vm);
-        return max_i32((int)h.x, (int)h.y);
-    } else {
-        return (int)vm;
-    }
-}
 
 // Copy a wave's m keys (src, LDS) into the workgroup area behind what other
 // waves have added (one LDS atomic for the wave's base).  Sets sh.overflow if
@@ -196,11 +114,6 @@ __device__ __noinline__ uint32_t exact_scan_wave(uint64_t* wb, uint64_t* out, co
         f(ex, ex != 0);
     };
     return wave_exact_topk<DT::kOrderBits>(wb, kWaveCap, out, visit, k);
-}
-
-// Device-scope load of a published key (bypasses the non-coherent L2).
-__device__ __forceinline__ uint64_t load_published(const uint64_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Selection by the last workgroup of a column: the top k of the S*k
@@ -344,7 +257,16 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
         bool neg_nan;
         lane_stats<DT, NV>(d, vmax, rep, neg_nan);
         if (ex) rep = max_u32(rep, key_order(ex));
+        // Each wave's k-th largest lane maximum bounds the workgroup's k-th
+        // largest element from below, so the largest of the four does too.
+        // (For k = 1 a wave's own maximum already leaves only its ties.)
         uint32_t T = wave_kth_largest<OB>(rep, k);
+        if (k > 1) {
+            if ((tid & 63u) == 0) sh.wave_thr[wave] = T;
+            __syncthreads();
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) T = max_u32(T, sh.wave_thr[w]);
+        }
         if (nbest == k) T = max_u32(T, key_order(t_run));
         const uint64_t tc = max_u64((uint64_t)T << 32, nbest == k ? t_run + 1 : (uint64_t)0);
 
@@ -353,6 +275,8 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
         if (!exact) {
             RawFilter<DT> f;
             f.set(T);
+          if constexpr (NV <= 2) {
+            // few vectors per lane: test them in place
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
                 const bool pv = i < nvalid && (!f.positive || vec_max_signed<DT>(vmax[i]) >= (int)f.lo);
@@ -372,6 +296,50 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
                     }
                 }
             }
+          } else {
+            // Vectors whose maximum reaches T go to the wave's queue; the
+            // queue is drained one vector per lane, and the elements at or
+            // above T become keys.
+            u32x4* qd = sh.qdata[wave];
+            uint32_t* qv = sh.qvec[wave];
+            const uint32_t lane = tid & 63u;
+            uint32_t qcnt = 0;  // wave-uniform
+            auto drain = [&]() {
+                for (uint32_t b = 0; b < qcnt; b += 64u) {
+                    const uint32_t e = b + lane;
+                    u32x4 v = {0u, 0u, 0u, 0u};
+                    uint32_t m = 0, row0 = 0;
+                    if (e < qcnt) {
+                        v = qd[e];
+                        row0 = head + qv[e] * EPV;
+#pragma unroll
+                        for (int el = 0; el < EPV; ++el) m |= f.pass(vec_elem<DT>(v, el)) ? (1u << el) : 0u;
+                    }
+                    while (__any(m != 0)) {
+                        const uint32_t el = m != 0 ? (uint32_t)__builtin_ctz(m) : 0u;
+                        const uint64_t key = make_key(DT::order(vec_elem_dyn<DT>(v, el)), row0 + el, tag);
+                        cnt = wave_append(wb, cnt, kWaveCap, m != 0 && key >= tc, key);
+                        m &= m - 1u;
+                    }
+                }
+                qcnt = 0;
+            };
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const bool pv = i < nvalid && (!f.positive || vec_max_signed<DT>(vmax[i]) >= (int)f.lo);
+                const unsigned long long bal = __ballot(pv);
+                if (bal) {
+                    if (pv) {
+                        const uint32_t pos = qcnt + lanes_below(bal);
+                        qd[pos] = d[i];
+                        qv[pos] = v0 + (uint32_t)i * kBlock;
+                    }
+                    qcnt += (uint32_t)__popcll(bal);
+                    if (qcnt > (uint32_t)(kQueue - 64)) drain();
+                }
+            }
+            drain();
+          }
             if (wave == 0) cnt = wave_append(wb, cnt, kWaveCap, ex != 0 && ex >= tc, ex);
             exact = cnt > (uint32_t)kWaveCap;
         }
@@ -424,8 +392,9 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
 
     // ---- the column's last workgroup: select from the S published lists ----
     merge_lists<DT>(a, sh, parts);
+    const uint64_t* top = sh.best;
     if (tid < k) {
-        const uint64_t key = sh.best[tid];
+        const uint64_t key = top[tid];
         const uint32_t row = key_row(key), o = key_order(key);
         static_cast<storage*>(a.out_values)[(int64_t)c * k + tid] =
             (storage)((o == DT::kZeroOrder || o == DT::kNanOrder) ? (uint32_t)col[row]

@@ -18,6 +18,7 @@ struct topk_cols {
     int64_t segments;   // workgroups per column
     int64_t blocks;     // workgroups of the main kernel
     int64_t tiles;      // column tiles (row-interleaved layout)
+    int32_t algo;       // topk_algo of the column-contiguous layout
     int nv;             // 16-byte vectors (row steps) per lane per pass
     void* workspace;    // tickets, then the published lists (C*S*k keys)
     size_t workspace_bytes;
@@ -70,6 +71,34 @@ int choose_row_nv(int64_t V, int64_t S) {
     return ceil_div(V, S) <= 256 ? 8 : 16;
 }
 
+// One wave per vocabulary segment pays off once the columns alone give every
+// CU a workgroup or so: then no column needs a deep split, and waves that
+// never wait for each other keep the memory system busy.
+#ifndef TOPK_WAVE_MIN_COLUMNS
+#define TOPK_WAVE_MIN_COLUMNS (1 << 30)
+#endif
+
+bool wave_fits(int64_t S, int32_t k) { return S * topk::kColWavesPerBlock * k <= topk::kWaveSegMergeKeys; }
+
+// Workgroups per column for the wave-segment kernel: about one workgroup per
+// CU overall, at least 64 vectors per wave, and the merge within its limit.
+int64_t choose_wave_segments(int64_t V, int64_t C, int dtype, int32_t k, int cu_count) {
+    const int64_t nvec = vectors_per_column(V, dtype);
+    int64_t s = ceil_div(cu_count, C);
+    const int64_t most = nvec / (kMinVecsPerSegment * topk::kColWavesPerBlock);
+    if (s > most) s = most;
+    while (s > 1 && !wave_fits(s, k)) --s;
+    return s < 1 ? 1 : s;
+}
+
+// Smallest vector count per lane that covers a wave segment in one pass, else 8.
+int choose_wave_nv(int64_t V, int64_t S, int dtype) {
+    const int64_t per_wave = ceil_div(vectors_per_column(V, dtype), S * topk::kColWavesPerBlock);
+    for (int nv : topk::kColVecChoices)
+        if (per_wave <= 64 * nv) return nv;
+    return topk::kColVecChoices[2];
+}
+
 // Smallest vector count per lane that covers a segment in one pass.
 int choose_col_nv(int64_t V, int64_t S, int dtype) {
     const int64_t per_block = ceil_div(vectors_per_column(V, dtype), S);
@@ -79,7 +108,7 @@ int choose_col_nv(int64_t V, int64_t S, int dtype) {
 }
 
 int create_impl(topk_cols_t* out, int64_t V, int64_t C, int32_t k, int32_t dtype, int32_t layout,
-                int64_t ld, int64_t forced_segments) {
+                int64_t ld, int64_t forced_segments, int32_t algo) {
     if (!out) return TOPK_ERR_INVALID_ARG;
     *out = nullptr;
     if (V < 1 || C < 1 || k < 1 || (int64_t)k > V) return TOPK_ERR_INVALID_ARG;
@@ -88,10 +117,14 @@ int create_impl(topk_cols_t* out, int64_t V, int64_t C, int32_t k, int32_t dtype
     if (layout == TOPK_COL_CONTIG && ld < V) return TOPK_ERR_INVALID_ARG;
     if (layout == TOPK_ROW_INTERLEAVED && ld < C) return TOPK_ERR_INVALID_ARG;
     if (forced_segments < 0) return TOPK_ERR_INVALID_ARG;
+    if (algo != TOPK_ALGO_AUTO && algo != TOPK_ALGO_WORKGROUP && algo != TOPK_ALGO_WAVE) return TOPK_ERR_INVALID_ARG;
     if (k > TOPK_MAX_K || V > TOPK_MAX_V) return TOPK_ERR_UNSUPPORTED;
     if (forced_segments > topk::kMaxSegments) return TOPK_ERR_UNSUPPORTED;
     const bool row = layout == TOPK_ROW_INTERLEAVED;
+    if (row && algo != TOPK_ALGO_AUTO) return TOPK_ERR_UNSUPPORTED;
     if (row && forced_segments * k > topk::kRowMaxMergeKeys) return TOPK_ERR_UNSUPPORTED;
+    if (!row && algo == TOPK_ALGO_WAVE && forced_segments > 0 && !wave_fits(forced_segments, k))
+        return TOPK_ERR_UNSUPPORTED;
 
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess) return TOPK_ERR_HIP;
@@ -100,22 +133,31 @@ int create_impl(topk_cols_t* out, int64_t V, int64_t C, int32_t k, int32_t dtype
         cu_count < 1)
         return TOPK_ERR_HIP;
 
+    if (!row && algo == TOPK_ALGO_AUTO) {
+        algo = C >= TOPK_WAVE_MIN_COLUMNS ? TOPK_ALGO_WAVE : TOPK_ALGO_WORKGROUP;
+        if (algo == TOPK_ALGO_WAVE && forced_segments > 0 && !wave_fits(forced_segments, k))
+            algo = TOPK_ALGO_WORKGROUP;
+    }
+    const bool wave = !row && algo == TOPK_ALGO_WAVE;
     const int64_t tiles = row ? ceil_div(C, topk::row_tile_columns(dtype)) : 0;
     const int64_t S = forced_segments > 0 ? forced_segments
-                      : row ? choose_row_segments(V, tiles, k, cu_count)
-                            : choose_col_segments(V, C, dtype, cu_count);
+                      : row  ? choose_row_segments(V, tiles, k, cu_count)
+                      : wave ? choose_wave_segments(V, C, dtype, k, cu_count)
+                             : choose_col_segments(V, C, dtype, cu_count);
     const int64_t blocks = row ? tiles * S : C * S;
     if (blocks > 0x7FFFFFFF) return TOPK_ERR_UNSUPPORTED;
+    const int64_t lists = wave ? S * topk::kColWavesPerBlock : S;  // published lists per column
 
     const size_t ticket_bytes =
         row ? 0 : ((size_t)C * topk::kTicketStride * sizeof(uint32_t) + 255) & ~(size_t)255;
-    const size_t ws_bytes = ticket_bytes + (size_t)C * (size_t)S * (size_t)k * sizeof(uint64_t);
+    const size_t ws_bytes = ticket_bytes + (size_t)C * (size_t)lists * (size_t)k * sizeof(uint64_t);
 
     topk_cols* h = new (std::nothrow) topk_cols();
     if (!h) return TOPK_ERR_OUT_OF_MEMORY;
     h->V = V; h->C = C; h->ld = ld; h->k = k; h->dtype = dtype; h->layout = layout;
     h->device = device; h->segments = S; h->blocks = blocks; h->tiles = tiles;
-    h->nv = row ? choose_row_nv(V, S) : choose_col_nv(V, S, dtype);
+    h->algo = row ? (int32_t)TOPK_ALGO_AUTO : algo;
+    h->nv = row ? choose_row_nv(V, S) : wave ? choose_wave_nv(V, S, dtype) : choose_col_nv(V, S, dtype);
     h->workspace_bytes = ws_bytes;
     hipError_t e = hipMalloc(&h->workspace, ws_bytes);
     if (e != hipSuccess) {
@@ -140,12 +182,17 @@ extern "C" {
 
 int topk_cols_create(topk_cols_t* out, int64_t V, int64_t C, int32_t k, int32_t dtype,
                      int32_t layout, int64_t ld) {
-    return create_impl(out, V, C, k, dtype, layout, ld, 0);
+    return create_impl(out, V, C, k, dtype, layout, ld, 0, TOPK_ALGO_AUTO);
 }
 
 int topk_cols_create_with_segments(topk_cols_t* out, int64_t V, int64_t C, int32_t k,
                                    int32_t dtype, int32_t layout, int64_t ld, int64_t segments) {
-    return create_impl(out, V, C, k, dtype, layout, ld, segments);
+    return create_impl(out, V, C, k, dtype, layout, ld, segments, TOPK_ALGO_AUTO);
+}
+
+int topk_cols_create_tuned(topk_cols_t* out, int64_t V, int64_t C, int32_t k, int32_t dtype,
+                           int32_t layout, int64_t ld, int64_t segments, int32_t algo) {
+    return create_impl(out, V, C, k, dtype, layout, ld, segments, algo);
 }
 
 int topk_cols_run(topk_cols_t h, const void* logits, void* out_values, int32_t* out_ids,
@@ -184,7 +231,8 @@ int topk_cols_run(topk_cols_t h, const void* logits, void* out_values, int32_t* 
         a.tickets = h->tickets;
         a.out_values = out_values;
         a.out_ids = out_ids;
-        e = topk::launch_col(h->dtype, h->nv, a, stream);
+        e = h->algo == TOPK_ALGO_WAVE ? topk::launch_colw(h->dtype, h->nv, a, stream)
+                                      : topk::launch_col(h->dtype, h->nv, a, stream);
     }
     if (e != hipSuccess) return TOPK_ERR_HIP;
     ++h->runs;
@@ -210,8 +258,10 @@ const char* topk_cols_status_string(int status) {
     }
 }
 
-int topk_cols_query(topk_cols_t h, int64_t* segments, int64_t* blocks, int64_t* workspace_bytes) {
+int topk_cols_query(topk_cols_t h, int64_t* segments, int64_t* blocks, int64_t* workspace_bytes,
+                    int32_t* algo) {
     if (!h) return TOPK_ERR_INVALID_ARG;
+    if (algo) *algo = h->algo;
     if (segments) *segments = h->segments;
     if (blocks) *blocks = h->blocks;
     if (workspace_bytes) *workspace_bytes = (int64_t)h->workspace_bytes;

@@ -38,6 +38,13 @@ constexpr int kColVecChoices[3] = {2, 4, 8};
 // dtype: TOPK_BF16 or TOPK_F32; nv: one of kColVecChoices.
 hipError_t launch_col(int dtype, int nv, const ColArgs& a, hipStream_t stream);
 
+// Column-contiguous, one wave per vocabulary segment: the same arguments,
+// with S workgroups per column and 4*S wave segments, each publishing a list
+// (partials holds C*4*S*k keys).  The last wave of a column merges
+// 4*S*k <= kWaveSegMergeKeys keys.
+constexpr int kWaveSegMergeKeys = 2048;
+hipError_t launch_colw(int dtype, int nv, const ColArgs& a, hipStream_t stream);
+
 // Row-interleaved launch: element (r, c) at x[r*ld + c].  The scan grid is
 // tiles*S workgroups: workgroup b handles row segment b / tiles and column
 // tile b % tiles (128 bytes of each row); a second kernel merges each

@@ -30,8 +30,10 @@ TOPK_MAX_V = (1 << 24) - 1
 DTYPES = {"bf16": 0, "f32": 1}
 LAYOUTS = {"col": 0, "row": 1}
 
-EXPORTED = ("topk_cols_create", "topk_cols_create_with_segments", "topk_cols_run",
-            "topk_cols_destroy", "topk_cols_status_string", "topk_cols_query")
+EXPORTED = ("topk_cols_create", "topk_cols_create_with_segments", "topk_cols_create_tuned",
+            "topk_cols_run", "topk_cols_destroy", "topk_cols_status_string", "topk_cols_query")
+# kernel families of the column-contiguous layout
+ALGOS = {"auto": 0, "workgroup": 1, "wave": 2}
 
 _lib = None
 
@@ -55,13 +57,16 @@ def load(path: str = LIBRARY):
     lib.topk_cols_create.restype = ctypes.c_int
     lib.topk_cols_create_with_segments.argtypes = [ctypes.POINTER(p), i64, i64, i32, i32, i32, i64, i64]
     lib.topk_cols_create_with_segments.restype = ctypes.c_int
+    lib.topk_cols_create_tuned.argtypes = [ctypes.POINTER(p), i64, i64, i32, i32, i32, i64, i64, i32]
+    lib.topk_cols_create_tuned.restype = ctypes.c_int
     lib.topk_cols_run.argtypes = [p, p, p, p, p]
     lib.topk_cols_run.restype = ctypes.c_int
     lib.topk_cols_destroy.argtypes = [p]
     lib.topk_cols_destroy.restype = ctypes.c_int
     lib.topk_cols_status_string.argtypes = [ctypes.c_int]
     lib.topk_cols_status_string.restype = ctypes.c_char_p
-    lib.topk_cols_query.argtypes = [p, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.topk_cols_query.argtypes = [p, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                    ctypes.POINTER(i32)]
     lib.topk_cols_query.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -80,24 +85,26 @@ class TopkCols:
     """One top-k shape on the current GPU (a handle of the C library)."""
 
     def __init__(self, V: int, C: int, k: int, dtype: str = "bf16", layout: str = "col",
-                 ld: int | None = None, segments: int = 0):
-        if dtype not in DTYPES or layout not in LAYOUTS:
-            raise ValueError(f"dtype must be one of {list(DTYPES)}, layout one of {list(LAYOUTS)}")
+                 ld: int | None = None, segments: int = 0, algo: str = "auto"):
+        if dtype not in DTYPES or layout not in LAYOUTS or algo not in ALGOS:
+            raise ValueError(f"dtype must be one of {list(DTYPES)}, layout one of {list(LAYOUTS)}, "
+                             f"algo one of {list(ALGOS)}")
         self.V, self.C, self.k, self.dtype, self.layout = V, C, k, dtype, layout
         self.ld = ld if ld is not None else (V if layout == "col" else C)
         lib = load()
         self._h = ctypes.c_void_p()
-        rc = lib.topk_cols_create_with_segments(ctypes.byref(self._h), V, C, k, DTYPES[dtype],
-                                                LAYOUTS[layout], self.ld, segments)
+        rc = lib.topk_cols_create_tuned(ctypes.byref(self._h), V, C, k, DTYPES[dtype],
+                                        LAYOUTS[layout], self.ld, segments, ALGOS[algo])
         if rc != TOPK_OK:
             raise TopkError(rc, "topk_cols_create")
 
     def query(self) -> dict:
-        s, b, w = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
-        rc = load().topk_cols_query(self._h, ctypes.byref(s), ctypes.byref(b), ctypes.byref(w))
+        s, b, w, a = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+        rc = load().topk_cols_query(self._h, ctypes.byref(s), ctypes.byref(b), ctypes.byref(w), ctypes.byref(a))
         if rc != TOPK_OK:
             raise TopkError(rc, "topk_cols_query")
-        return {"segments": s.value, "blocks": b.value, "workspace_bytes": w.value}
+        names = {v: n for n, v in ALGOS.items()}
+        return {"segments": s.value, "blocks": b.value, "workspace_bytes": w.value, "algo": names.get(a.value)}
 
     def run_ptr(self, x_ptr: int, values_ptr: int, ids_ptr: int, stream_ptr: int) -> None:
         """Enqueue one run on raw device pointers and a raw HIP stream handle."""

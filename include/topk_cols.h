@@ -123,17 +123,36 @@ const char *topk_cols_status_string(int status);
 int topk_cols_create_with_segments(topk_cols_t *out, int64_t V, int64_t C, int32_t k,
                                    int32_t dtype, int32_t layout, int64_t ld, int64_t segments);
 
+/* Kernel families of the column-contiguous layout (topk_cols_create_tuned). */
+typedef enum {
+    TOPK_ALGO_AUTO = 0,       /* chosen from the shape */
+    TOPK_ALGO_WORKGROUP = 1,  /* a workgroup per vocabulary segment */
+    TOPK_ALGO_WAVE = 2        /* a wave per vocabulary segment (4 per workgroup) */
+} topk_algo;
+
+/*
+ * Like topk_cols_create_with_segments, with the kernel family fixed as well
+ * (column-contiguous layout; the row-interleaved layout accepts only
+ * TOPK_ALGO_AUTO).  For tests and tuning: every family gives the same result.
+ * With TOPK_ALGO_WAVE, 4 * segments * k above 2048 returns
+ * TOPK_ERR_UNSUPPORTED.  An unknown algo returns TOPK_ERR_INVALID_ARG.
+ */
+int topk_cols_create_tuned(topk_cols_t *out, int64_t V, int64_t C, int32_t k, int32_t dtype,
+                           int32_t layout, int64_t ld, int64_t segments, int32_t algo);
+
 /*
  * Introspection for tests and benchmarks.  Writes the launch decomposition
  * chosen at create.
  * segments: workgroups per column (vocabulary-axis split) for the
- *           column-contiguous kernel, or row segments for the interleaved one.
+ *           column-contiguous kernels, or row segments for the interleaved one.
  * blocks: total workgroups of the scan kernel (the row-interleaved layout
  *         adds a merge kernel of ceil(C / 4) workgroups).
  * workspace_bytes: device bytes owned by the handle.
+ * algo: the topk_algo in use (TOPK_ALGO_AUTO for the row-interleaved layout).
  * Any output pointer may be NULL.
  */
-int topk_cols_query(topk_cols_t h, int64_t *segments, int64_t *blocks, int64_t *workspace_bytes);
+int topk_cols_query(topk_cols_t h, int64_t *segments, int64_t *blocks, int64_t *workspace_bytes,
+                    int32_t *algo);
 
 #ifdef __cplusplus
 }

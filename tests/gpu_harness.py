@@ -25,10 +25,10 @@ def to_device(torch, x, offset=0):
     return buf[offset:offset + flat.size]
 
 
-def run_gpu(gpu, x, V, C, k, dtype, layout, ld, segments=0, offset=0, repeat=1):
+def run_gpu(gpu, x, V, C, k, dtype, layout, ld, segments=0, offset=0, repeat=1, algo="auto"):
     torch, T = gpu
     dx = to_device(torch, x, offset)
-    with T.TopkCols(V, C, k, dtype, layout, ld, segments=segments) as h:
+    with T.TopkCols(V, C, k, dtype, layout, ld, segments=segments, algo=algo) as h:
         for _ in range(repeat):
             v, i = h.run(dx)
         torch.cuda.synchronize()
@@ -40,8 +40,8 @@ def run_oracle(x, V, C, k, dtype, layout, ld, nthreads=8):
     return oracle.topk_cols(x, V, C, k, ODT[dtype], OLY[layout], ld, nthreads=nthreads)
 
 
-def assert_parity(gpu, x, V, C, k, dtype, layout, ld, segments=0, offset=0, label=""):
-    gv, gi = run_gpu(gpu, x, V, C, k, dtype, layout, ld, segments=segments, offset=offset)
+def assert_parity(gpu, x, V, C, k, dtype, layout, ld, segments=0, offset=0, label="", algo="auto"):
+    gv, gi = run_gpu(gpu, x, V, C, k, dtype, layout, ld, segments=segments, offset=offset, algo=algo)
     ov, oi = run_oracle(x, V, C, k, dtype, layout, ld)
     bad = np.flatnonzero((gi != oi).any(axis=1) | (bits(gv) != bits(ov)).any(axis=1))
     assert bad.size == 0, (f"{label}: {bad.size} of {C} columns differ; first column {bad[0]}: "

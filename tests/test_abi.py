@@ -89,6 +89,19 @@ def test_negative_segments_refused(lib):
     assert rc == T.TOPK_ERR_UNSUPPORTED and h.value is None
 
 
+def test_tuned_create_checks_its_arguments(lib):
+    def tuned(*args):
+        h = ctypes.c_void_p(0xDEAD)
+        rc = lib.topk_cols_create_tuned(ctypes.byref(h), *args)
+        return rc, h
+    rc, h = tuned(100, 7, 8, 0, 0, 100, 0, 3)           # unknown algorithm
+    assert rc == T.TOPK_ERR_INVALID_ARG and h.value is None
+    rc, h = tuned(100, 448, 8, 0, 1, 448, 0, 2)         # row-interleaved takes only "auto"
+    assert rc == T.TOPK_ERR_UNSUPPORTED and h.value is None
+    rc, h = tuned(100000, 56, 64, 0, 0, 100000, 9, 2)   # wave merge: 4*9*64 > 2048 keys
+    assert rc == T.TOPK_ERR_UNSUPPORTED and h.value is None
+
+
 def test_null_out_pointer_refused(lib):
     assert lib.topk_cols_create(None, 10, 7, 1, 0, 0, 10) == T.TOPK_ERR_INVALID_ARG
 
@@ -96,7 +109,7 @@ def test_null_out_pointer_refused(lib):
 def test_null_handle_calls(lib):
     assert lib.topk_cols_destroy(None) == T.TOPK_OK
     assert lib.topk_cols_run(None, 16, 16, 16, None) == T.TOPK_ERR_INVALID_ARG
-    assert lib.topk_cols_query(None, None, None, None) == T.TOPK_ERR_INVALID_ARG
+    assert lib.topk_cols_query(None, None, None, None, None) == T.TOPK_ERR_INVALID_ARG
 
 
 def test_valid_create_without_a_device_fails_cleanly(lib):
