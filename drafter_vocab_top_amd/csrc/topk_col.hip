@@ -62,6 +62,7 @@ constexpr int kBlockCap = 512;               // carried best + candidates per wo
 constexpr int kMergeKeysPerThread = 16;      // S*k <= 4096 published keys, 16 per thread
 constexpr int kSpinLimit = 1 << 16;          // about 0.1 s: a store that has not landed by then never will
 constexpr int kQueue = 128;                  // queued vectors per wave
+constexpr int kWaveMergeKeys = 1024;         // wave 0 alone merges up to this many published keys
 
 struct ColShared {
     alignas(16) uint64_t cand[kBlockCap];          // [0, nbest) carried best, then candidates
@@ -194,6 +195,63 @@ __device__ __forceinline__ void merge_lists(const ColArgs& a, ColShared& sh, con
     __syncthreads();
 }
 
+// Selection by wave 0 of the column's last workgroup when the S*k published
+// keys fit 16 per lane (coalesced device-scope loads): the k-th largest lane
+// maximum is the threshold, the keys at or above it are ranked (through
+// scalar broadcasts when at most 64), and out(position, key) writes each of
+// the top k.
+template <class DT, class Out>
+__device__ __forceinline__ void merge_lists_wave(const ColArgs& a, ColShared& sh, const uint64_t* parts,
+                                                 const Out& out) {
+    constexpr int OB = DT::kOrderBits;
+    constexpr int RMAX = kWaveMergeKeys / 64;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t k = (uint32_t)a.k, tag = a.tag;
+    const uint32_t M = (uint32_t)a.S * k;
+    const uint32_t R = (M + 63u) / 64u;  // wave-uniform
+    uint64_t keys[RMAX];
+#pragma unroll
+    for (int j = 0; j < RMAX; ++j) {
+        const uint32_t idx = (uint32_t)j * 64u + lane;
+        keys[j] = 0;
+        if ((uint32_t)j < R && idx < M) keys[j] = load_published(parts + idx);
+    }
+#pragma unroll
+    for (int j = 0; j < RMAX; ++j) {
+        const uint32_t idx = (uint32_t)j * 64u + lane;
+        if ((uint32_t)j < R && idx < M) {
+            for (int spin = 0; key_tag(keys[j]) != tag && spin < kSpinLimit; ++spin) {
+                __builtin_amdgcn_s_sleep(1);
+                keys[j] = load_published(parts + idx);
+            }
+        }
+    }
+    uint64_t rep = 0;
+#pragma unroll
+    for (int j = 0; j < RMAX; ++j)
+        if ((uint32_t)j < R) rep = max_u64(rep, keys[j]);
+    const uint32_t T = wave_kth_largest<OB>(key_order(rep), k);
+    // sentinel keys (order 0, from segments with fewer than k rows) never qualify
+    auto visit = [&](auto&& f) {
+#pragma unroll
+        for (int j = 0; j < RMAX; ++j)
+            if ((uint32_t)j < R) f(keys[j], key_order(keys[j]) != 0);
+    };
+    uint32_t cnt = 0;
+    visit([&](uint64_t key, bool valid) {
+        cnt = wave_append(sh.cand, cnt, kBlockCap, valid && key_order(key) >= T, key);
+    });
+    if (cnt <= 64u) {
+        const uint64_t key = lane < cnt ? sh.cand[lane] : 0ull;
+        const uint32_t r = wave_rank_of(key, cnt);
+        if (lane < cnt && r < k) out(r, key);
+        return;
+    }
+    const uint32_t n = cnt > (uint32_t)kBlockCap ? wave_exact_topk<OB>(sh.wbuf[0], kWaveCap, sh.best, visit, k)
+                                                 : wave_rank_select(sh.cand, cnt, k, sh.best);
+    if (lane < n) out(lane, sh.best[lane]);
+}
+
 template <class DT, int NV>
 __global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
     using storage = typename DT::storage;
@@ -236,6 +294,7 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
     uint64_t* wb = sh.wbuf[wave];
     uint32_t nbest = 0;  // the segment's best so far, in sh.cand[0..nbest) at the start of a pass
     uint64_t t_run = 0;  // the k-th best key once nbest == k
+    uint32_t n_last = 0; // candidates of the last pass, in sh.cand
     const uint32_t per_pass = (uint32_t)kBlock * NV;
     const uint32_t npass = ve > vb ? (ve - vb + per_pass - 1) / per_pass : 1u;
 
@@ -365,41 +424,61 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
             __syncthreads();
             n = sh.ncand;
         }
-        rank_select(sh.cand, n, k, sh.best, tid, kBlock);
-        __syncthreads();
-        nbest = min_u32(n, k);
-        if (nbest == k) t_run = sh.best[k - 1];
         if (p + 1 < npass) {
+            rank_select(sh.cand, n, k, sh.best, tid, kBlock);
+            __syncthreads();
+            nbest = min_u32(n, k);
+            if (nbest == k) t_run = sh.best[k - 1];
             if (tid < nbest) sh.cand[tid] = sh.best[tid];
             if (tid == 0) sh.ncand = nbest;
             __syncthreads();
+        } else {
+            n_last = n;
         }
     }
 
-    // ---- publish the segment's sorted list, then take the column's ticket ----
+    // ---- wave 0: rank the segment's candidates, publish the sorted list and
+    //      take the column's ticket (the stores precede the ticket in the
+    //      wave's program order) ----
     const uint64_t sentinel = tag;  // order 0: below every real key
     uint64_t* parts = a.partials + (int64_t)c * S * k;
-    if (tid < k)  // wave 0 (k <= 64): the stores precede the ticket in program order
-        __hip_atomic_store(&parts[s * k + tid], tid < nbest ? sh.best[tid] : sentinel,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (tid == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(&a.tickets[c * kTicketStride], 1u,
-                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sh.is_last = old == S - 1u ? 1u : 0u;
+    if (wave == 0) {
+        const uint32_t lane = tid;
+        uint64_t* dst = parts + s * k;
+        if (n_last <= 64u) {
+            const uint64_t key = lane < n_last ? sh.cand[lane] : 0ull;
+            const uint32_t r = wave_rank_of(key, n_last);
+            if (lane < n_last && r < k)
+                __hip_atomic_store(&dst[r], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            const uint32_t m = wave_rank_select(sh.cand, n_last, k, sh.best);
+            if (lane < m) __hip_atomic_store(&dst[lane], sh.best[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (lane >= min_u32(n_last, k) && lane < k)
+            __hip_atomic_store(&dst[lane], sentinel, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) {
+            const uint32_t old = __hip_atomic_fetch_add(&a.tickets[c * kTicketStride], 1u,
+                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            sh.is_last = old == S - 1u ? 1u : 0u;
+        }
     }
     __syncthreads();
     if (!sh.is_last) return;
 
     // ---- the column's last workgroup: select from the S published lists ----
-    merge_lists<DT>(a, sh, parts);
-    const uint64_t* top = sh.best;
-    if (tid < k) {
-        const uint64_t key = top[tid];
+    auto write_out = [&](uint32_t pos, uint64_t key) {
         const uint32_t row = key_row(key), o = key_order(key);
-        static_cast<storage*>(a.out_values)[(int64_t)c * k + tid] =
+        static_cast<storage*>(a.out_values)[(int64_t)c * k + pos] =
             (storage)((o == DT::kZeroOrder || o == DT::kNanOrder) ? (uint32_t)col[row]
                                                                   : DT::bits_from_order(o));
-        a.out_ids[(int64_t)c * k + tid] = (int32_t)row;
+        a.out_ids[(int64_t)c * k + pos] = (int32_t)row;
+    };
+    if ((uint32_t)a.S * k <= (uint32_t)kWaveMergeKeys) {
+        if (wave != 0) return;
+        merge_lists_wave<DT>(a, sh, parts, write_out);
+    } else {
+        merge_lists<DT>(a, sh, parts);
+        if (tid < k) write_out(tid, sh.best[tid]);
     }
     if (tid == 0)
         __hip_atomic_store(&a.tickets[c * kTicketStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

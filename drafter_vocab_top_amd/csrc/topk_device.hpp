@@ -190,6 +190,29 @@ __device__ __forceinline__ uint32_t rank_select(const uint64_t* keys, uint32_t n
     return min_u32(n, k);
 }
 
+// Rank of each lane's key among the keys of lanes 0..n-1 (n <= 64,
+// wave-uniform): the number of them that are larger.  Keys are broadcast one
+// lane at a time through scalar registers, so there is no LDS traffic; four
+// independent chains per step hide the scalar-read latency.  Lanes at or
+// past n get a rank as well; callers ignore it.
+__device__ __forceinline__ uint32_t wave_rank_of(uint64_t key, uint32_t n) {
+    const int hi = (int)(uint32_t)(key >> 32), lo = (int)(uint32_t)key;
+    auto lane_key = [&](uint32_t j) {
+        return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(hi, (int)j) << 32) |
+               (uint32_t)__builtin_amdgcn_readlane(lo, (int)j);
+    };
+    uint32_t r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+    uint32_t j = 0;
+    for (; j + 4 <= n; j += 4) {
+        r0 += lane_key(j) > key ? 1u : 0u;
+        r1 += lane_key(j + 1) > key ? 1u : 0u;
+        r2 += lane_key(j + 2) > key ? 1u : 0u;
+        r3 += lane_key(j + 3) > key ? 1u : 0u;
+    }
+    for (; j < n; ++j) r0 += lane_key(j) > key ? 1u : 0u;
+    return r0 + r1 + r2 + r3;
+}
+
 // Rank selection by one wave (see rank_select).
 __device__ __forceinline__ uint32_t wave_rank_select(const uint64_t* keys, uint32_t n, uint32_t k,
                                                      uint64_t* out) {
