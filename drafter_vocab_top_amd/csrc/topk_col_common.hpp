@@ -101,4 +101,14 @@ __device__ __forceinline__ uint64_t load_published(const uint64_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// A lower bound of the k-th largest of the lanes' orders for thresholds:
+// exact for 16-bit orders; for 32-bit orders the search runs on the upper 16
+// bits and the bound is rounded down to a multiple of 2^16 (half the rounds,
+// and rounding down keeps it a lower bound).
+template <class DT>
+__device__ __forceinline__ uint32_t wave_kth_bound(uint32_t order, uint32_t k) {
+    if constexpr (DT::kOrderBits == 16) return wave_kth_largest<16>(order, k);
+    else return wave_kth_largest<16>(order >> 16, k) << 16;
+}
+
 }  // namespace topk

@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kBlock) void topk_colw_kernel(ColArgs a) {
         bool neg_nan;
         lane_stats<DT, NV>(cur, vmax, rep, neg_nan);
         if (ex) rep = max_u32(rep, key_order(ex));
-        uint32_t T = wave_kth_largest<OB>(rep, k);
+        uint32_t T = wave_kth_bound<DT>(rep, k);
         if (nbest == k) T = max_u32(T, key_order(t_run));
         const uint64_t tc = max_u64((uint64_t)T << 32, nbest == k ? t_run + 1 : (uint64_t)0);
 
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(kBlock) void topk_colw_kernel(ColArgs a) {
 #pragma unroll
     for (int j = 0; j < kWMergePerLane; ++j)
         if ((uint32_t)j < R) rep = max_u64(rep, keys[j]);
-    const uint32_t T = wave_kth_largest<OB>(key_order(rep), k);
+    const uint32_t T = wave_kth_bound<DT>(key_order(rep), k);
     // sentinel keys (order 0, from segments with fewer than k rows) never qualify
     auto visit = [&](auto&& f) {
 #pragma unroll

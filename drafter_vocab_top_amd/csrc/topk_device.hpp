@@ -111,7 +111,9 @@ struct RawFilter {
             span = DT::kRawMask;
             positive = false;
         } else if (T > DT::kZeroOrder) {
-            lo = (T == DT::kNanOrder) ? DT::kFirstNan : T - DT::kZeroOrder;
+            // above the order of +Inf only NaNs qualify (a rounded-down bound
+            // may fall between the two)
+            lo = (T > DT::kZeroOrder + (DT::kFirstNan - 1u)) ? DT::kFirstNan : T - DT::kZeroOrder;
             span = (DT::kSignBit - 1u) - lo;
             positive = true;
         } else {
