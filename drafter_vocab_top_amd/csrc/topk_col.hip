@@ -149,7 +149,7 @@ __device__ __forceinline__ void merge_lists(const ColArgs& a, ColShared& sh, con
 #pragma unroll
     for (int j = 0; j < kMergeKeysPerThread; ++j)
         if ((uint32_t)j < J) rep = max_u64(rep, keys[j]);
-    const uint32_t wt = wave_kth_largest<OB>(key_order(rep), k);
+    const uint32_t wt = wave_kth_bound<DT>(key_order(rep), k);
     if (lane == 0) sh.wave_thr[wave] = wt;
     if (tid == 0) {
         sh.ncand = 0;
@@ -230,7 +230,7 @@ __device__ __forceinline__ void merge_lists_wave(const ColArgs& a, ColShared& sh
 #pragma unroll
     for (int j = 0; j < RMAX; ++j)
         if ((uint32_t)j < R) rep = max_u64(rep, keys[j]);
-    const uint32_t T = wave_kth_largest<OB>(key_order(rep), k);
+    const uint32_t T = wave_kth_bound<DT>(key_order(rep), k);
     // sentinel keys (order 0, from segments with fewer than k rows) never qualify
     auto visit = [&](auto&& f) {
 #pragma unroll
@@ -319,7 +319,7 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
         // Each wave's k-th largest lane maximum bounds the workgroup's k-th
         // largest element from below, so the largest of the four does too.
         // (For k = 1 a wave's own maximum already leaves only its ties.)
-        uint32_t T = wave_kth_largest<OB>(rep, k);
+        uint32_t T = wave_kth_bound<DT>(rep, k);
         if (k > 1) {
             if ((tid & 63u) == 0) sh.wave_thr[wave] = T;
             __syncthreads();
