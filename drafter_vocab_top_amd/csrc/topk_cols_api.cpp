@@ -214,6 +214,7 @@ int topk_cols_run(topk_cols_t h, const void* logits, void* out_values, int32_t* 
         a.S = (int32_t)h->segments;
         a.tiles = (int32_t)h->tiles;
         a.vec_loads = ((uintptr_t)logits % 16 == 0 && (h->ld * (int64_t)es) % 16 == 0) ? 1 : 0;
+        a.key32 = (h->dtype == TOPK_BF16 && ceil_div(h->V, h->segments) <= 65536) ? 1 : 0;
         a.partials = h->partials;
         a.out_values = out_values;
         a.out_ids = out_ids;

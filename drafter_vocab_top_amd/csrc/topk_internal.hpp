@@ -58,6 +58,7 @@ struct RowArgs {
     int32_t S;            // row segments; S*k <= kRowMaxMergeKeys
     int32_t tiles;        // column tiles
     int32_t vec_loads;    // 1 if every row start of a tile is 16-byte aligned
+    int32_t key32;        // 1: bf16 and segments of at most 65,536 rows (32-bit candidate keys)
     uint64_t* partials;   // C*S*k keys
     void* out_values;     // C*k elements of the input dtype
     int32_t* out_ids;     // C*k

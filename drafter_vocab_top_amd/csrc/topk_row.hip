@@ -75,11 +75,37 @@ struct RowTile {
     static constexpr int TPC = kBlock / TW;                                     // threads per column
 };
 
-template <class DT, int CAP>
+// Candidate keys of the scan.  RowKey64 is the library's 64-bit key.
+// RowKey32 (bf16, segments of at most 65,536 rows) keeps the 16-bit order in
+// bits 31..16 and 0xFFFF - (row - r_lo) in bits 15..0: the same order, half
+// the LDS, so twice the candidates fit.  Keys are widened to 64 bits when a
+// segment's list is written.  A zero key is never a real one.
+struct RowKey64 {
+    using T = uint64_t;
+    static constexpr int kPad = 2;  // keeps rows 16-byte aligned, spreads banks
+    __device__ __forceinline__ static T make(uint32_t order, uint32_t row, uint32_t) { return make_key(order, row, 0u); }
+    __device__ __forceinline__ static uint32_t order(T key) { return key_order(key); }
+    __device__ __forceinline__ static uint32_t row(T key, uint32_t) { return key_row(key); }
+    __device__ __forceinline__ static uint64_t wide(T key, uint32_t) { return key; }
+};
+struct RowKey32 {
+    using T = uint32_t;
+    static constexpr int kPad = 4;
+    __device__ __forceinline__ static T make(uint32_t order, uint32_t row, uint32_t r_lo) {
+        return (order << 16) | (0xFFFFu - (row - r_lo));
+    }
+    __device__ __forceinline__ static uint32_t order(T key) { return key >> 16; }
+    __device__ __forceinline__ static uint32_t row(T key, uint32_t r_lo) { return r_lo + 0xFFFFu - (key & 0xFFFFu); }
+    __device__ __forceinline__ static uint64_t wide(T key, uint32_t r_lo) {
+        return key ? make_key(key >> 16, row(key, r_lo), 0u) : 0ull;
+    }
+};
+
+template <class DT, int CAP, class KT>
 struct RowShared {
     static constexpr int TW = RowTile<DT>::TW;
-    static constexpr int STRIDE = CAP + 2;       // keys per column; the padding spreads LDS banks
-    alignas(16) uint64_t cand[TW][STRIDE];       // per-column candidate keys
+    static constexpr int STRIDE = CAP + KT::kPad;  // keys per column row
+    alignas(16) typename KT::T cand[TW][STRIDE];   // per-column candidate keys
     alignas(16) uint64_t tmp[kWaves][kMaxK];     // exact-path output per wave
     alignas(16) u32x4 qdata[kWaves][kRowQueue];  // queued row vectors
     uint32_t qmeta[kWaves][kRowQueue];           // (row << 3) | lane group of each queued vector
@@ -308,9 +334,9 @@ __device__ __noinline__ uint32_t exact_row_column(const typename DT::storage* x,
 // TPC threads (consecutive lanes of one wave); thread q holds candidates q,
 // q + TPC, ...  Returns the new count and sets T_out to that k-th largest
 // order (thr when n <= k).
-template <class DT, int CAP>
-__device__ __forceinline__ uint32_t trim_column(uint64_t* cand, uint32_t q, uint32_t n, uint32_t k, uint32_t thr,
-                                                uint32_t* T_out) {
+template <class DT, int CAP, class KT>
+__device__ __forceinline__ uint32_t trim_column(typename KT::T* cand, uint32_t q, uint32_t n, uint32_t k,
+                                                uint32_t thr, uint32_t* T_out) {
     constexpr int TPC = RowTile<DT>::TPC;
     constexpr int VPT = CAP / TPC;
     uint32_t o[VPT];
@@ -318,7 +344,7 @@ __device__ __forceinline__ uint32_t trim_column(uint64_t* cand, uint32_t q, uint
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
         const uint32_t idx = q + (uint32_t)v * TPC;
-        o[v] = idx < n ? key_order(cand[idx]) : 0u;
+        o[v] = idx < n ? KT::order(cand[idx]) : 0u;
         mx = max_u32(mx, o[v]);
     }
     uint32_t T = thr;
@@ -336,64 +362,91 @@ __device__ __forceinline__ uint32_t trim_column(uint64_t* cand, uint32_t q, uint
         const uint32_t idx = q + (uint32_t)v * TPC;
         const bool keep = idx < n && o[v] >= T;
         const uint64_t bal = __ballot(keep) & gmask;
-        const uint64_t key = keep ? cand[idx] : 0ull;
+        const typename KT::T key = keep ? cand[idx] : (typename KT::T)0;
         if (keep) cand[out + (uint32_t)__popcll(bal & below)] = key;
         out += (uint32_t)__popcll(bal);
     }
     return out;
 }
 
-template <class DT, int NV, int CAP>
-__device__ __noinline__ void rebuild_column(RowShared<DT, CAP>& sh, const typename DT::storage* x, int64_t ld,
-                                            uint32_t colx, uint32_t col, uint32_t pass_lo, uint32_t pass_hi,
-                                            uint32_t k) {
+// Rank count over the keys of one column (thread first, first + stride, ...
+// each take a key; all read the same keys with 16-byte LDS reads): the key
+// of rank r < k goes, widened, to dst[r].  Keys are readable up to n rounded
+// up to 8.
+template <class KT>
+__device__ __forceinline__ void rank_keys(const typename KT::T* keys, uint32_t n, uint32_t k, uint64_t* dst,
+                                          uint32_t first, uint32_t stride, uint32_t r_lo) {
+    using T = typename KT::T;
+    typedef T vec2 __attribute__((ext_vector_type(16 / sizeof(T))));
+    constexpr uint32_t PER = 16 / sizeof(T);  // keys per 16-byte read
+    const uint32_t n8 = (n + 7u) & ~7u;
+    for (uint32_t t = first; t < n; t += stride) {
+        const T key = keys[t];
+        uint32_t r = 0;
+        for (uint32_t j = 0; j < n8; j += 8) {
+#pragma unroll
+            for (uint32_t h = 0; h < 8; h += PER) {
+                const vec2 q = *reinterpret_cast<const vec2*>(keys + j + h);
+#pragma unroll
+                for (uint32_t e = 0; e < PER; ++e) r += (q[e] > key && j + h + e < n) ? 1u : 0u;
+            }
+        }
+        if (r < k) dst[r] = KT::wide(key, r_lo);
+    }
+}
+
+template <class DT, int NV, int CAP, class KT>
+__device__ __noinline__ void rebuild_column(RowShared<DT, CAP, KT>& sh, const typename DT::storage* x, int64_t ld,
+                                            uint32_t colx, uint32_t col, uint32_t r_lo, uint32_t pass_lo,
+                                            uint32_t pass_hi, uint32_t k) {
     using F = RowFilter<DT>;
+    using T = typename KT::T;
     constexpr int PRE = (CAP + 63) / 64;             // buffer keys per lane
     constexpr int PER = kRowsPerStep * NV / 64;      // pass rows per lane
     constexpr int OB = DT::kOrderBits;
     const uint32_t lane = threadIdx.x & 63u;
-    uint64_t key[PRE + PER];
+    T key[PRE + PER];
     bool valid[PRE + PER];
 #pragma unroll
     for (int j = 0; j < PRE; ++j) {
         const uint32_t idx = (uint32_t)j * 64u + lane;
-        key[j] = idx < (uint32_t)CAP ? sh.cand[colx][idx] : 0ull;
-        valid[j] = idx < (uint32_t)CAP && key_row(key[j]) < pass_lo;
+        key[j] = idx < (uint32_t)CAP ? sh.cand[colx][idx] : (T)0;
+        valid[j] = idx < (uint32_t)CAP && KT::row(key[j], r_lo) < pass_lo;
     }
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         const uint32_t r = pass_lo + (uint32_t)j * 64u + lane;
         valid[PRE + j] = r < pass_hi;
         const uint32_t raw = r < pass_hi ? (uint32_t)x[(int64_t)r * ld + col] : 0u;
-        key[PRE + j] = make_key(DT::order(raw), r, 0u);
+        key[PRE + j] = KT::make(DT::order(raw), r, r_lo);
     }
-    uint32_t T = 0;
+    uint32_t T_k = 0;
 #pragma unroll 1
     for (int b = OB - 1; b >= 0; --b) {
-        const uint32_t c = T | (1u << b);
+        const uint32_t c = T_k | (1u << b);
         uint32_t n = 0;
 #pragma unroll
-        for (int j = 0; j < PRE + PER; ++j) n += (uint32_t)__popcll(__ballot(valid[j] && key_order(key[j]) >= c));
-        if (n >= k) T = c;
+        for (int j = 0; j < PRE + PER; ++j) n += (uint32_t)__popcll(__ballot(valid[j] && KT::order(key[j]) >= c));
+        if (n >= k) T_k = c;
     }
     uint32_t cnt = 0;
 #pragma unroll
     for (int j = 0; j < PRE + PER; ++j)
-        cnt = wave_append(sh.cand[colx], cnt, CAP, valid[j] && key_order(key[j]) >= T, key[j]);
+        cnt = wave_append(sh.cand[colx], cnt, (uint32_t)CAP, valid[j] && KT::order(key[j]) >= T_k, key[j]);
     if (lane == 0) {
         sh.cnt[colx] = cnt;
         if (cnt > (uint32_t)CAP) sh.flag[colx] |= 1u;
-        if (T > sh.thr[colx]) {
+        if (T_k > sh.thr[colx]) {
             uint32_t fmv, fqv;
-            F::encode(T, fmv, fqv);
-            sh.thr[colx] = T;
+            F::encode(T_k, fmv, fqv);
+            sh.thr[colx] = T_k;
             sh.fm[colx] = (typename DT::storage)fmv;
             sh.fq[colx] = (typename DT::storage)fqv;
         }
     }
 }
 
-template <class DT, int NV, int CAP>
+template <class DT, int NV, int CAP, class KT>
 __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
     using storage = typename DT::storage;
     using F = RowFilter<DT>;
@@ -402,10 +455,12 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
     constexpr int TPC = RowTile<DT>::TPC;
     constexpr int OB = DT::kOrderBits;
     static_assert(NV % 2 == 0, "two row groups per pass");
-    __shared__ RowShared<DT, CAP> sh;
+    __shared__ RowShared<DT, CAP, KT> sh;
 
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
     const uint32_t k = (uint32_t)a.k;
+    // trim a column above this many candidates (room for a pass's new ones)
+    const uint32_t trim_at = max_u32(2u * k, max_u32(24u, (uint32_t)CAP - 32u));
     const uint32_t tiles = (uint32_t)a.tiles;
     const uint32_t S = (uint32_t)a.S;
     const uint32_t s = blockIdx.x / tiles;          // row segment
@@ -486,7 +541,7 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
                     const uint32_t col = gg * CPV + j;
                     const uint32_t o = DT::order(row_elem<DT>(d, j));
                     const uint32_t pos = atomicAdd(&sh.cnt[col], 1u);
-                    if (pos < (uint32_t)CAP) sh.cand[col][pos] = make_key(o, row, 0u);
+                    if (pos < (uint32_t)CAP) sh.cand[col][pos] = KT::make(o, row, r_lo);
                 }
             }
         }
@@ -584,9 +639,9 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
         //     than max(2k, 24) keys is trimmed to its running top-k
         {
             const uint32_t n = sh.cnt[pcol];
-            if (p + 1 < npass && n <= (uint32_t)CAP && n > max_u32(2u * k, 24u)) {
+            if (p + 1 < npass && n <= (uint32_t)CAP && n > trim_at) {
                 uint32_t T;
-                const uint32_t kept = trim_column<DT, CAP>(sh.cand[pcol], pq, n, k, sh.thr[pcol], &T);
+                const uint32_t kept = trim_column<DT, CAP, KT>(sh.cand[pcol], pq, n, k, sh.thr[pcol], &T);
                 if (pq == 0) {
                     sh.cnt[pcol] = kept;
                     if (T > sh.thr[pcol]) {
@@ -606,7 +661,7 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
             while (todo) {
                 const uint32_t colx = wave + (uint32_t)__builtin_ctzll(todo) * kWaves;
                 todo &= todo - 1ull;
-                rebuild_column<DT, NV, CAP>(sh, x, a.ld, colx, c0 + colx, pass_lo, pass_hi, k);
+                rebuild_column<DT, NV, CAP, KT>(sh, x, a.ld, colx, c0 + colx, r_lo, pass_lo, pass_hi, k);
             }
         }
         if (p + 1 < npass) {
@@ -629,15 +684,15 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
         const uint32_t col = c0 + pcol;
         const uint32_t n = sh.cnt[pcol];
         if (col < C && sh.flag[pcol] == 0u && n <= (uint32_t)CAP) {
-            uint64_t* cand = sh.cand[pcol];
+            typename KT::T* cand = sh.cand[pcol];
             uint32_t kept = n;
             if (n > max_u32(2u * k, 32u)) {  // many left: trim to k plus ties first
                 uint32_t T;
-                kept = trim_column<DT, CAP>(cand, pq, n, k, sh.thr[pcol], &T);
+                kept = trim_column<DT, CAP, KT>(cand, pq, n, k, sh.thr[pcol], &T);
             }
             // rank what is left and write the top k, sorted, to the segment's list
             uint64_t* dst = lists + ((int64_t)col * S + s) * k;
-            rank_select(cand, kept, k, dst, pq, TPC);
+            rank_keys<KT>(cand, kept, k, dst, pq, TPC, r_lo);
             for (uint32_t t = kept + pq; t < k; t += TPC) dst[t] = 0ull;
         }
     }
@@ -649,7 +704,9 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
         const uint32_t colx = wave + (uint32_t)__builtin_ctzll(todo) * kWaves;
         todo &= todo - 1ull;
         const uint32_t col = c0 + colx;
-        const uint32_t n = exact_row_column<DT>(x, a.ld, col, r_lo, r_hi, sh.cand[colx], CAP, sh.tmp[wave], k);
+        // the wave's queue area (idle by now) is the exact search's scratch
+        const uint32_t n = exact_row_column<DT>(x, a.ld, col, r_lo, r_hi, reinterpret_cast<uint64_t*>(sh.qdata[wave]),
+                                                2u * kRowQueue, sh.tmp[wave], k);
         uint64_t* dst = lists + ((int64_t)col * S + s) * k;
         if (lane < k) dst[lane] = lane < n ? sh.tmp[wave][lane] : 0ull;
     }
@@ -703,12 +760,12 @@ __global__ __launch_bounds__(kBlock) void topk_row_merge(RowArgs a) {
     }
 }
 
-template <class DT, int CAP>
+template <class DT, int CAP, class KT>
 hipError_t launch_scan(int nv, const RowArgs& a, hipStream_t stream) {
     const dim3 grid((uint32_t)((int64_t)a.tiles * a.S)), block(kBlock);
     switch (nv) {
-        case 8: hipLaunchKernelGGL((topk_row_scan<DT, 8, CAP>), grid, block, 0, stream, a); break;
-        case 16: hipLaunchKernelGGL((topk_row_scan<DT, 16, CAP>), grid, block, 0, stream, a); break;
+        case 8: hipLaunchKernelGGL((topk_row_scan<DT, 8, CAP, KT>), grid, block, 0, stream, a); break;
+        case 16: hipLaunchKernelGGL((topk_row_scan<DT, 16, CAP, KT>), grid, block, 0, stream, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -716,8 +773,18 @@ hipError_t launch_scan(int nv, const RowArgs& a, hipStream_t stream) {
 
 template <class DT>
 hipError_t launch_row_dt(int nv, const RowArgs& a, hipStream_t stream) {
-    const hipError_t e = a.k <= kRowSmallK ? launch_scan<DT, kRowCapSmall>(nv, a, stream)
-                                           : launch_scan<DT, kRowCapLarge>(nv, a, stream);
+    hipError_t e;
+    if constexpr (DT::kOrderBits == 16) {
+        if (a.key32)
+            e = a.k <= kRowSmallK ? launch_scan<DT, 2 * kRowCapSmall, RowKey32>(nv, a, stream)
+                                  : launch_scan<DT, kRowCapLarge, RowKey32>(nv, a, stream);
+        else
+            e = a.k <= kRowSmallK ? launch_scan<DT, kRowCapSmall, RowKey64>(nv, a, stream)
+                                  : launch_scan<DT, kRowCapLarge, RowKey64>(nv, a, stream);
+    } else {
+        e = a.k <= kRowSmallK ? launch_scan<DT, kRowCapSmall, RowKey64>(nv, a, stream)
+                              : launch_scan<DT, kRowCapLarge, RowKey64>(nv, a, stream);
+    }
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((topk_row_merge<DT>), dim3((uint32_t)((a.C + kWaves - 1) / kWaves)), dim3(kBlock), 0,
                        stream, a);
