@@ -24,6 +24,7 @@ struct topk_cols {
     size_t workspace_bytes;
     uint32_t* tickets;
     uint64_t* partials;
+    uint32_t* bound;    // row layout: per-column lower bounds shared by the segments
     uint32_t runs;      // completed run() calls, for the run tag
 };
 
@@ -150,7 +151,9 @@ int create_impl(topk_cols_t* out, int64_t V, int64_t C, int32_t k, int32_t dtype
 
     const size_t ticket_bytes =
         row ? 0 : ((size_t)C * topk::kTicketStride * sizeof(uint32_t) + 255) & ~(size_t)255;
-    const size_t ws_bytes = ticket_bytes + (size_t)C * (size_t)lists * (size_t)k * sizeof(uint64_t);
+    const size_t list_bytes = ((size_t)C * (size_t)lists * (size_t)k * sizeof(uint64_t) + 255) & ~(size_t)255;
+    const size_t bound_bytes = row ? (size_t)C * topk::kRowBoundSlots * sizeof(uint32_t) : 0;
+    const size_t ws_bytes = ticket_bytes + list_bytes + bound_bytes;
 
     topk_cols* h = new (std::nothrow) topk_cols();
     if (!h) return TOPK_ERR_OUT_OF_MEMORY;
@@ -167,6 +170,7 @@ int create_impl(topk_cols_t* out, int64_t V, int64_t C, int32_t k, int32_t dtype
     }
     h->tickets = row ? nullptr : static_cast<uint32_t*>(h->workspace);
     h->partials = reinterpret_cast<uint64_t*>(static_cast<char*>(h->workspace) + ticket_bytes);
+    h->bound = row ? reinterpret_cast<uint32_t*>(static_cast<char*>(h->workspace) + ticket_bytes + list_bytes) : nullptr;
     if (hipMemset(h->workspace, 0, ws_bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
         (void)hipFree(h->workspace);
         delete h;
@@ -216,6 +220,8 @@ int topk_cols_run(topk_cols_t h, const void* logits, void* out_values, int32_t* 
         a.vec_loads = ((uintptr_t)logits % 16 == 0 && (h->ld * (int64_t)es) % 16 == 0) ? 1 : 0;
         a.key32 = (h->dtype == TOPK_BF16 && ceil_div(h->V, h->segments) <= 65536) ? 1 : 0;
         a.partials = h->partials;
+        a.bound = h->bound;
+        a.use_bound = h->k <= topk::kRowBoundSlots ? 1 : 0;
         a.out_values = out_values;
         a.out_ids = out_ids;
         e = topk::launch_row(h->dtype, h->nv, a, stream);

@@ -60,11 +60,14 @@ struct RowArgs {
     int32_t vec_loads;    // 1 if every row start of a tile is 16-byte aligned
     int32_t key32;        // 1: bf16 and segments of at most 65,536 rows (32-bit candidate keys)
     uint64_t* partials;   // C*S*k keys
+    uint32_t* bound;      // C*kRowBoundSlots orders, zero between runs (see the row scan)
+    int32_t use_bound;    // 1 if k <= kRowBoundSlots: segments share a lower bound per column
     void* out_values;     // C*k elements of the input dtype
     int32_t* out_ids;     // C*k
 };
 
 constexpr int kRowMaxMergeKeys = 1024;
+constexpr int kRowBoundSlots = 16;
 
 // Columns per tile for a dtype (128 bytes of a row).
 int row_tile_columns(int dtype);

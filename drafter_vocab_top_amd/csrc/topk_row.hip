@@ -11,7 +11,10 @@
 // first, ties to the smaller row (ignis "DFlash2" page, "How it works").
 //
 // Scan kernel.  A pass is NV steps of 32 rows, and the next pass's loads are
-// issued before the current pass is filtered.  Every column keeps a running
+// issued before the current pass is filtered.  In a whole tile of aligned
+// rows every load is unconditional (rows past the segment are clamped and
+// masked), so the compiler can count the loads in flight and filtering waits
+// for the current pass only.  Every column keeps a running
 // threshold T_c (an order that is at most the segment's k-th largest) and an
 // LDS buffer of candidate keys that holds every element seen so far at or
 // above T_c.
@@ -27,6 +30,14 @@
 //     When the queue fills, and at the end of the pass, the wave turns the
 //     queued vectors into keys, one vector per lane, and adds them to the
 //     column buffers (an LDS atomic per key).
+//  2b. Segments of one column share a lower bound on the column's k-th
+//     largest order over all V rows.  After step 1 each workgroup publishes
+//     its column maximum (an atomic max into slot s mod k of the column, in
+//     the workspace); every pass reads the k slots before its prefetch and,
+//     once all are filled, raises T_c to their minimum: k elements of
+//     distinct segments are at least that large.  This bound is far above a
+//     single segment's own, so after the first passes almost nothing passes
+//     the filter.  The merge kernel clears the slots for the next run.
 //  3. After a pass, a column holding more than max(2k, 24) keys is trimmed:
 //     the threads of the column find the exact k-th largest order among its
 //     candidates, which becomes the new T_c, and compact the buffer in place.
@@ -46,6 +57,8 @@
 // partial lists (each lane holds a contiguous run of them; the k-th largest
 // of the lanes' maxima is the threshold, then a rank count) and writes the
 // output.  The kernel boundary orders it after the scan.
+#include <type_traits>
+
 #include "topk_device.hpp"
 #include "topk_internal.hpp"
 
@@ -547,29 +560,82 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
         }
     };
 
-    u32x4 cur[NV], nxt[NV];
-    if (npass > 0) load_pass(cur, 0);
+    // A whole tile of 16-byte aligned rows loads with no per-lane branch:
+    // rows past the segment re-read its last row and are masked where they
+    // are used, and after the last pass a dummy prefetch re-reads the
+    // segment's first rows. With every load unconditional the compiler knows
+    // how many loads are in flight, so filtering a pass waits for that pass
+    // alone while the next one streams in.
+    const bool full_tile = a.vec_loads != 0 && c0 + (uint32_t)TW <= C;
+    auto load_full = [&](u32x4(&d)[NV], uint32_t p, uint32_t step) {
+        const uint32_t rbase = r_lo + p * per_pass + rsub;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const uint32_t r = min_u32(rbase + (uint32_t)i * step, r_hi - 1u);
+            d[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + (int64_t)r * a.ld + cg));
+        }
+    };
+    const u32x4 fill4 = u32x4{DT::kFillDword, DT::kFillDword, DT::kFillDword, DT::kFillDword};
+
+    // Lower bound shared by the segments of a column: slot j holds the
+    // largest group maximum published so far by a segment s with s mod k = j
+    // (zero if none yet).  Distinct slots hold elements of distinct segments,
+    // so once all k slots are filled their minimum is at most the column's
+    // k-th largest order over all V rows: no element below it can be in the
+    // output, whatever segment it lies in.  The merge kernel zeroes the slots
+    // for the next run.
+    constexpr int kBoundPerThread = kRowBoundSlots / TPC;
+    const uint32_t* bound_col = a.bound + (int64_t)min_u32(c0 + pcol, C - 1u) * kRowBoundSlots;
+
     uint32_t nanacc[4] = {0u, 0u, 0u, 0u};
+    auto scan_passes = [&](auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    u32x4 cur[NV], nxt[NV];
+    if (npass > 0) {
+        if constexpr (FULL)
+            load_full(cur, 0, kRowsPerStep);
+        else
+            load_pass(cur, 0);
+    }
     __syncthreads();
 
     for (uint32_t p = 0; p < npass; ++p) {
-        if (p + 1 < npass) load_pass(nxt, p + 1);
+        // the column's shared slots, read before the prefetch so that waiting
+        // for them does not wait for the next pass
+        uint32_t slot[kBoundPerThread];
+#pragma unroll
+        for (int j = 0; j < kBoundPerThread; ++j)
+            slot[j] = __hip_atomic_load(&bound_col[pq * kBoundPerThread + (uint32_t)j], __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+        if constexpr (FULL) {
+            const bool more = p + 1 < npass;
+            load_full(nxt, more ? p + 1 : 0u, more ? (uint32_t)kRowsPerStep : 0u);
+        } else {
+            if (p + 1 < npass) load_pass(nxt, p + 1);
+        }
 
         if (p == 0) {
             // (1) starting thresholds from 64 group maxima per column
             ColMax<DT> m0, m1;
             m0.init();
             m1.init();
+            // rows past the segment count as -Inf (a full tile loaded copies of its last row)
+            auto row_vec = [&](const u32x4& v, uint32_t pp, int i) {
+                if constexpr (FULL)
+                    return r_lo + pp * per_pass + rsub + (uint32_t)i * kRowsPerStep < r_hi ? v : fill4;
+                else
+                    return v;
+            };
 #pragma unroll
             for (int i = 0; i < NV; i += 2) {
-                m0.add(cur[i]);
-                m1.add(cur[i + 1]);
+                m0.add(row_vec(cur[i], 0u, i));
+                m1.add(row_vec(cur[i + 1], 0u, i + 1));
             }
             if (npass > 1) {  // the second pass is already loaded: group maxima over both
 #pragma unroll
                 for (int i = 0; i < NV; i += 2) {
-                    m0.add(nxt[i]);
-                    m1.add(nxt[i + 1]);
+                    m0.add(row_vec(nxt[i], 1u, i));
+                    m1.add(row_vec(nxt[i + 1], 1u, i + 1));
                 }
             }
 #pragma unroll
@@ -589,13 +655,18 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
                 vmax = max_u32(vmax, v[j]);
             }
             // all 64 are >= the minimum, and k <= 64
-            const uint32_t T = group_kth<TPC, RPT>(v, k, group_min<TPC>(vmin), group_max<TPC>(vmax));
+            const uint32_t cmax = group_max<TPC>(vmax);
+            const uint32_t T = group_kth<TPC, RPT>(v, k, group_min<TPC>(vmin), cmax);
             if (pq == 0) {
                 uint32_t fmv, fqv;
                 F::encode(T, fmv, fqv);
                 sh.thr[pcol] = T;
                 sh.fm[pcol] = (storage)fmv;
                 sh.fq[pcol] = (storage)fqv;
+                // publish an element of this segment (at least as large as cmax) in slot s mod k
+                if (a.use_bound && c0 + pcol < C)
+                    __hip_atomic_fetch_max(&a.bound[(c0 + pcol) * kRowBoundSlots + s % k], cmax, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
             }
             __syncthreads();
         }
@@ -653,6 +724,19 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
                     }
                 }
             }
+            // the shared bound, once every one of the k slots is filled
+            uint32_t bmin = 0xFFFFFFFFu;
+#pragma unroll
+            for (int j = 0; j < kBoundPerThread; ++j)
+                if (pq * kBoundPerThread + (uint32_t)j < k) bmin = min_u32(bmin, slot[j]);
+            const uint32_t Tg = group_min<TPC>(bmin);
+            if (a.use_bound && pq == 0 && p + 1 < npass && Tg > sh.thr[pcol]) {
+                uint32_t fmv, fqv;
+                F::encode(Tg, fmv, fqv);
+                sh.thr[pcol] = Tg;
+                sh.fm[pcol] = (storage)fmv;
+                sh.fq[pcol] = (storage)fqv;
+            }
             const uint32_t pass_lo = r_lo + p * per_pass;
             const uint32_t pass_hi = min_u32(pass_lo + per_pass, r_hi);
             uint64_t todo = wave_columns<TW>(wave, [&](uint32_t colx) {
@@ -670,6 +754,11 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
             for (int i = 0; i < NV; ++i) cur[i] = nxt[i];
         }
     }
+    };
+    if (full_tile)
+        scan_passes(std::integral_constant<bool, true>{});
+    else
+        scan_passes(std::integral_constant<bool, false>{});
 
     // columns that hold a negative NaN take the exact path
 #pragma unroll
@@ -725,6 +814,8 @@ __global__ __launch_bounds__(kBlock) void topk_row_merge(RowArgs a) {
     if (col >= (uint32_t)a.C) return;
     const uint32_t k = (uint32_t)a.k, S = (uint32_t)a.S, M = S * k;
     const uint64_t* src = a.partials + (int64_t)col * M;
+    // the scan is over: clear the column's shared-bound slots for the next run
+    if (a.use_bound && lane < (uint32_t)kRowBoundSlots) a.bound[(int64_t)col * kRowBoundSlots + lane] = 0u;
     // Each lane takes a contiguous run of the sorted segment lists, so a
     // lane's maximum is a segment maximum (k <= 16) and the k-th largest lane
     // maximum is a tight threshold.

@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 
 from drafter_vocab_top_amd import workloads as W
-from gpu_harness import assert_parity
+from gpu_harness import assert_parity, run_oracle, to_device
+from topk_checks import bits
 
 pytestmark = pytest.mark.gpu
 
@@ -97,3 +98,30 @@ def test_exhaustive_small_alphabet_rows(gpu):
     x = np.ascontiguousarray(cols.T)
     for k in range(1, 7):
         assert_parity(gpu, x, 6, n, k, W.BF16, W.ROW, n, label=f"row exhaustive k={k}")
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+def test_handle_reuse_across_inputs(gpu, dtype):
+    """Segments of a column share a lower bound on its k-th largest element
+    during a run.  One handle runs a matrix of large values, then matrices of
+    small values: every run must match the oracle on its own input (nothing
+    of an earlier run may carry over), including when the earlier run ended
+    on a different input."""
+    torch, T = gpu
+    V, C = 120011, 96
+    st = np.uint16 if dtype == W.BF16 else np.uint32
+    high = W.random_matrix(91, V, C, dtype, W.ROW, kind="normal")
+    low = W.random_matrix(92, V, C, dtype, W.ROW, kind="normal")
+    hf = W.float_view(high, dtype) + np.float32(64.0)
+    high = W.storage_from_bits(W.bf16_bits_from_f32(hf), dtype) if dtype == W.BF16 else hf.astype(np.float32)
+    for k in (1, 4, 16):
+        with T.TopkCols(V, C, k, dtype, W.ROW, C) as h:
+            for name, x in (("high", high), ("low", low), ("high", high), ("low", low)):
+                print(f"[parity-row] reuse k={k} {name} {dtype}", flush=True)
+                v, i = h.run(to_device(torch, x))
+                torch.cuda.synchronize()
+                gv = v.cpu().numpy().view(st).reshape(C, k)
+                gi = i.cpu().numpy().reshape(C, k)
+                ov, oi = run_oracle(x, V, C, k, dtype, W.ROW, C)
+                bad = np.flatnonzero((gi != oi).any(axis=1) | (bits(gv) != bits(ov)).any(axis=1))
+                assert bad.size == 0, f"reuse k={k} {name}: {bad.size} columns differ, first {bad[0]}"
