@@ -120,8 +120,8 @@ int create_impl(topk_cols_t* out, int64_t V, int64_t C, int32_t k, int32_t dtype
     if (forced_segments < 0) return TOPK_ERR_INVALID_ARG;
     if (algo != TOPK_ALGO_AUTO && algo != TOPK_ALGO_WORKGROUP && algo != TOPK_ALGO_WAVE) return TOPK_ERR_INVALID_ARG;
     if (k > TOPK_MAX_K || V > TOPK_MAX_V) return TOPK_ERR_UNSUPPORTED;
-    if (forced_segments > topk::kMaxSegments) return TOPK_ERR_UNSUPPORTED;
     const bool row = layout == TOPK_ROW_INTERLEAVED;
+    if (!row && forced_segments > topk::kMaxSegments) return TOPK_ERR_UNSUPPORTED;
     if (row && algo != TOPK_ALGO_AUTO) return TOPK_ERR_UNSUPPORTED;
     if (row && forced_segments * k > topk::kRowMaxMergeKeys) return TOPK_ERR_UNSUPPORTED;
     if (!row && algo == TOPK_ALGO_WAVE && forced_segments > 0 && !wave_fits(forced_segments, k))

@@ -382,6 +382,28 @@ __device__ __forceinline__ uint32_t trim_column(typename KT::T* cand, uint32_t q
     return out;
 }
 
+// Drops the candidates of one column whose order is below T (a raised
+// threshold), compacting the rest in place; the same thread layout as
+// trim_column.  Returns the new count.  n is column-uniform, so the loop
+// trip count is too.
+template <class DT, class KT>
+__device__ __forceinline__ uint32_t cull_column(typename KT::T* cand, uint32_t q, uint32_t n, uint32_t T) {
+    constexpr int TPC = RowTile<DT>::TPC;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint64_t gmask = ((1ull << TPC) - 1ull) << (lane & ~(uint32_t)(TPC - 1));
+    const uint64_t below = (1ull << lane) - 1ull;
+    uint32_t out = 0;
+    for (uint32_t base = 0; base < n; base += TPC) {
+        const uint32_t idx = base + q;
+        const typename KT::T key = idx < n ? cand[idx] : (typename KT::T)0;
+        const bool keep = idx < n && KT::order(key) >= T;
+        const uint64_t bal = __ballot(keep) & gmask;
+        if (keep) cand[out + (uint32_t)__popcll(bal & below)] = key;
+        out += (uint32_t)__popcll(bal);
+    }
+    return out;
+}
+
 // Rank count over the keys of one column (thread first, first + stride, ...
 // each take a key; all read the same keys with 16-byte LDS reads): the key
 // of rank r < k goes, widened, to dst[r].  Keys are readable up to n rounded
@@ -730,12 +752,18 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
             for (int j = 0; j < kBoundPerThread; ++j)
                 if (pq * kBoundPerThread + (uint32_t)j < k) bmin = min_u32(bmin, slot[j]);
             const uint32_t Tg = group_min<TPC>(bmin);
-            if (a.use_bound && pq == 0 && p + 1 < npass && Tg > sh.thr[pcol]) {
-                uint32_t fmv, fqv;
-                F::encode(Tg, fmv, fqv);
-                sh.thr[pcol] = Tg;
-                sh.fm[pcol] = (storage)fmv;
-                sh.fq[pcol] = (storage)fqv;
+            if (a.use_bound && p + 1 < npass && Tg > sh.thr[pcol]) {
+                // candidates below the raised threshold can go at once
+                const uint32_t nc = sh.cnt[pcol];
+                const uint32_t kept = nc <= (uint32_t)CAP ? cull_column<DT, KT>(sh.cand[pcol], pq, nc, Tg) : nc;
+                if (pq == 0) {
+                    uint32_t fmv, fqv;
+                    F::encode(Tg, fmv, fqv);
+                    sh.thr[pcol] = Tg;
+                    sh.fm[pcol] = (storage)fmv;
+                    sh.fq[pcol] = (storage)fqv;
+                    sh.cnt[pcol] = kept;
+                }
             }
             const uint32_t pass_lo = r_lo + p * per_pass;
             const uint32_t pass_hi = min_u32(pass_lo + per_pass, r_hi);
