@@ -54,9 +54,9 @@
 // re-read over the whole segment by one wave and selected by an exact search.
 //
 // Merge kernel: one wave per column selects the top k of its S sorted
-// partial lists (each lane holds a contiguous run of them; the k-th largest
-// of the lanes' maxima is the threshold, then a rank count) and writes the
-// output.  The kernel boundary orders it after the scan.
+// partial lists (read with coalesced loads; the k-th largest of the S list
+// heads is the threshold, then a rank count) and writes the output.  The
+// kernel boundary orders it after the scan.
 #include <type_traits>
 
 #include "topk_device.hpp"
@@ -406,11 +406,11 @@ __device__ __forceinline__ uint32_t cull_column(typename KT::T* cand, uint32_t q
 
 // Rank count over the keys of one column (thread first, first + stride, ...
 // each take a key; all read the same keys with 16-byte LDS reads): the key
-// of rank r < k goes, widened, to dst[r].  Keys are readable up to n rounded
-// up to 8.
+// of rank r < k goes, widened, to dst[r * dstride].  Keys are readable up to
+// n rounded up to 8.
 template <class KT>
 __device__ __forceinline__ void rank_keys(const typename KT::T* keys, uint32_t n, uint32_t k, uint64_t* dst,
-                                          uint32_t first, uint32_t stride, uint32_t r_lo) {
+                                          uint32_t dstride, uint32_t first, uint32_t stride, uint32_t r_lo) {
     using T = typename KT::T;
     typedef T vec2 __attribute__((ext_vector_type(16 / sizeof(T))));
     constexpr uint32_t PER = 16 / sizeof(T);  // keys per 16-byte read
@@ -426,7 +426,7 @@ __device__ __forceinline__ void rank_keys(const typename KT::T* keys, uint32_t n
                 for (uint32_t e = 0; e < PER; ++e) r += (q[e] > key && j + h + e < n) ? 1u : 0u;
             }
         }
-        if (r < k) dst[r] = KT::wide(key, r_lo);
+        if (r < k) dst[(int64_t)r * dstride] = KT::wide(key, r_lo);
     }
 }
 
@@ -809,7 +809,7 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
             }
             // rank what is left and write the top k, sorted, to the segment's list
             uint64_t* dst = lists + ((int64_t)col * S + s) * k;
-            rank_keys<KT>(cand, kept, k, dst, pq, TPC, r_lo);
+            rank_keys<KT>(cand, kept, k, dst, 1u, pq, TPC, r_lo);
             for (uint32_t t = kept + pq; t < k; t += TPC) dst[t] = 0ull;
         }
     }
@@ -844,18 +844,18 @@ __global__ __launch_bounds__(kBlock) void topk_row_merge(RowArgs a) {
     const uint64_t* src = a.partials + (int64_t)col * M;
     // the scan is over: clear the column's shared-bound slots for the next run
     if (a.use_bound && lane < (uint32_t)kRowBoundSlots) a.bound[(int64_t)col * kRowBoundSlots + lane] = 0u;
-    // Each lane takes a contiguous run of the sorted segment lists, so a
-    // lane's maximum is a segment maximum (k <= 16) and the k-th largest lane
-    // maximum is a tight threshold.
+    // Coalesced loads: load j gives lane l entry j*64 + l of the column's S
+    // lists.
     uint64_t keys[kRowMergeKeysPerLane];
 #pragma unroll
     for (int j = 0; j < kRowMergeKeysPerLane; ++j) {
-        const uint32_t idx = lane * kRowMergeKeysPerLane + (uint32_t)j;
+        const uint32_t idx = (uint32_t)j * 64u + lane;
         keys[j] = idx < M ? src[idx] : 0ull;
     }
+    // the threshold: k-th largest of the segment maxima (the head of each
+    // sorted list, lane l takes segments l, l + 64, ...)
     uint64_t rep = 0;
-#pragma unroll
-    for (int j = 0; j < kRowMergeKeysPerLane; ++j) rep = max_u64(rep, keys[j]);
+    for (uint32_t sg = lane; sg < S; sg += 64u) rep = max_u64(rep, src[sg * k]);
     const uint32_t T = wave_kth_largest<OB>(key_order(rep), k);
     auto visit = [&](auto&& f) {
 #pragma unroll
