@@ -59,7 +59,7 @@ int64_t choose_col_segments(int64_t V, int64_t C, int dtype, int cu_count) {
 // kTargetBlocksPerCU workgroups run per CU, each segment at least one
 // 32-row step, and the merge input S*k within its limit.
 int64_t choose_row_segments(int64_t V, int64_t tiles, int32_t k, int cu_count) {
-    int64_t s = ceil_div((int64_t)cu_count * kTargetBlocksPerCU, tiles);
+    int64_t s = (int64_t)cu_count * kTargetBlocksPerCU / tiles;  // no partial second wave
     const int64_t most_rows = V / 32;
     if (s > most_rows) s = most_rows;
     const int64_t merge_cap = topk::kRowMaxMergeKeys / k;

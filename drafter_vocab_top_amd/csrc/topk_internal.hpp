@@ -66,7 +66,7 @@ struct RowArgs {
     int32_t* out_ids;     // C*k
 };
 
-constexpr int kRowMaxMergeKeys = 1024;
+constexpr int kRowMaxMergeKeys = 2048;
 constexpr int kRowBoundSlots = 16;
 
 // Columns per tile for a dtype (128 bytes of a row).

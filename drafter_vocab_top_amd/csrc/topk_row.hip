@@ -71,7 +71,6 @@ constexpr int kRowsPerStep = kBlock / kRowLanesPerRow;  // 32 rows per workgroup
 constexpr int kRowTileBytes = 128;
 constexpr int kRowReps = 2 * kRowsPerStep;              // group maxima per column (first pass)
 constexpr int kRowQueue = 128;                          // queued row vectors per wave
-constexpr int kRowMergeKeysPerLane = kRowMaxMergeKeys / 64;
 // Candidate buffer per column: CAP keys.  A trim leaves about k of them and
 // is due above max(2k, 24), so a pass may add at least CAP - max(2k, 24)
 // (32 or more) before the buffer overflows.
@@ -830,7 +829,7 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
 }
 
 // One wave per column: the top k of the column's S partial lists.
-template <class DT>
+template <class DT, int KPL>
 __global__ __launch_bounds__(kBlock) void topk_row_merge(RowArgs a) {
     using storage = typename DT::storage;
     constexpr int OB = DT::kOrderBits;
@@ -846,9 +845,9 @@ __global__ __launch_bounds__(kBlock) void topk_row_merge(RowArgs a) {
     if (a.use_bound && lane < (uint32_t)kRowBoundSlots) a.bound[(int64_t)col * kRowBoundSlots + lane] = 0u;
     // Coalesced loads: load j gives lane l entry j*64 + l of the column's S
     // lists.
-    uint64_t keys[kRowMergeKeysPerLane];
+    uint64_t keys[KPL];
 #pragma unroll
-    for (int j = 0; j < kRowMergeKeysPerLane; ++j) {
+    for (int j = 0; j < KPL; ++j) {
         const uint32_t idx = (uint32_t)j * 64u + lane;
         keys[j] = idx < M ? src[idx] : 0ull;
     }
@@ -859,7 +858,7 @@ __global__ __launch_bounds__(kBlock) void topk_row_merge(RowArgs a) {
     const uint32_t T = wave_kth_largest<OB>(key_order(rep), k);
     auto visit = [&](auto&& f) {
 #pragma unroll
-        for (int j = 0; j < kRowMergeKeysPerLane; ++j) f(keys[j], key_order(keys[j]) != 0);
+        for (int j = 0; j < KPL; ++j) f(keys[j], key_order(keys[j]) != 0);
     };
     uint32_t cnt = 0;
     visit([&](uint64_t key, bool valid) { cnt = wave_append(buf[wave], cnt, kBuf, valid && key_order(key) >= T, key); });
@@ -905,8 +904,12 @@ hipError_t launch_row_dt(int nv, const RowArgs& a, hipStream_t stream) {
                               : launch_scan<DT, kRowCapLarge, RowKey64>(nv, a, stream);
     }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((topk_row_merge<DT>), dim3((uint32_t)((a.C + kWaves - 1) / kWaves)), dim3(kBlock), 0,
-                       stream, a);
+    // keys per lane: S*k entries over 64 lanes
+    const dim3 mgrid((uint32_t)((a.C + kWaves - 1) / kWaves));
+    if ((int64_t)a.S * a.k <= 1024)
+        hipLaunchKernelGGL((topk_row_merge<DT, 16>), mgrid, dim3(kBlock), 0, stream, a);
+    else
+        hipLaunchKernelGGL((topk_row_merge<DT, kRowMaxMergeKeys / 64>), mgrid, dim3(kBlock), 0, stream, a);
     return hipGetLastError();
 }
 

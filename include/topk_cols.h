@@ -68,7 +68,9 @@ typedef struct topk_cols *topk_cols_t;
  *
  * The handle owns a small device workspace: one partial list of k 8-byte
  * keys per column and vocabulary segment (C * segments * k keys) and, for the
- * column-contiguous layout, one 128-byte counter line per column.  Create
+ * column-contiguous layout, one 128-byte counter line per column, or, for
+ * the row-interleaved layout, 16 4-byte bound slots per column that the
+ * segments of a column share during a run.  Create
  * allocates it on the current device with hipMalloc, zeroes it and waits for
  * the zeroing to finish; create is not meant for the hot loop.
  *
@@ -116,9 +118,10 @@ const char *topk_cols_status_string(int status);
  * Like topk_cols_create, but with the vocabulary-axis split fixed to
  * `segments` workgroups per column (row segments for the interleaved layout)
  * instead of the automatic choice; 0 means automatic.  For tests and tuning:
- * the result is the same for every split.  segments above 64, or (for the
- * row-interleaved layout) segments * k above 1024, return
- * TOPK_ERR_UNSUPPORTED; negative values return TOPK_ERR_INVALID_ARG.
+ * the result is the same for every split.  For the column-contiguous
+ * layout segments above 64, and for the row-interleaved layout segments * k
+ * above 2048, return TOPK_ERR_UNSUPPORTED; negative values return
+ * TOPK_ERR_INVALID_ARG.
  */
 int topk_cols_create_with_segments(topk_cols_t *out, int64_t V, int64_t C, int32_t k,
                                    int32_t dtype, int32_t layout, int64_t ld, int64_t segments);

@@ -84,8 +84,8 @@ def test_negative_segments_refused(lib):
     assert rc == T.TOPK_ERR_INVALID_ARG and h.value is None
     rc, h = _create(lib, 100000, 7, 64, 0, 0, 100000, segments=65)
     assert rc == T.TOPK_ERR_UNSUPPORTED and h.value is None
-    # row-interleaved: the merge takes at most 1024 keys per column
-    rc, h = _create(lib, 100000, 448, 64, 0, 1, 448, segments=17)
+    # row-interleaved: the merge takes at most 2048 keys per column
+    rc, h = _create(lib, 100000, 448, 64, 0, 1, 448, segments=33)
     assert rc == T.TOPK_ERR_UNSUPPORTED and h.value is None
 
 

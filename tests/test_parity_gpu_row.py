@@ -47,12 +47,13 @@ def test_small_sweep(gpu, dtype, kind):
 
 @pytest.mark.parametrize("dtype", [W.BF16, W.F32])
 def test_every_segment_count(gpu, dtype):
-    """Any split of the rows gives the same answer (S*k <= 1024)."""
+    """Any split of the rows gives the same answer (S*k <= 2048; above 1024
+    the merge holds 32 keys per lane)."""
     V, C = 50021, 70
     x = W.random_matrix(78, V, C, dtype, W.ROW, kind="normal")
     for k in (1, 16, 64):
-        for seg in (1, 2, 3, 7, 16, 31, 64):
-            if seg * k > 1024:
+        for seg in (1, 2, 3, 7, 16, 31, 64, 73, 128, 1024):
+            if seg * k > 2048:
                 continue
             print(f"[parity-row] segments={seg} k={k} {dtype}", flush=True)
             assert_parity(gpu, x, V, C, k, dtype, W.ROW, C, segments=seg, label=f"row segments={seg} k={k}")
