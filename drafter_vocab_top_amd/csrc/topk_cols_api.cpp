@@ -47,7 +47,9 @@ int64_t choose_col_segments(int64_t V, int64_t C, int dtype, int cu_count) {
     const int64_t nvec = vectors_per_column(V, dtype);
     const int64_t max_nv = topk::kColVecChoices[2];
     int64_t s = ceil_div(nvec, kBlockThreads * max_nv);                 // one pass per workgroup
-    const int64_t fill = ceil_div((int64_t)cu_count * kTargetBlocksPerCU, C);
+    // about one workgroup per CU: more segments make the merge longer than
+    // they make the scan shorter
+    const int64_t fill = ceil_div((int64_t)cu_count, C);
     if (fill > s) s = fill;
     const int64_t most = nvec / kMinVecsPerSegment;                     // not too thin
     if (s > most) s = most;
