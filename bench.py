@@ -57,8 +57,8 @@ def log(*a):
 def kernel_sources_digest(layout: str = "col") -> str:
     """Digest of the sources that decide what the kernel of one layout does."""
     from drafter_vocab_top_amd import build as B
-    kernel = "topk_col.hip" if layout == "col" else "topk_row.hip"
-    names = (kernel, "topk_device.hpp", "topk_cols_api.cpp")
+    kernel = ("topk_col.hip", "topk_col_common.hpp") if layout == "col" else ("topk_row.hip",)
+    names = kernel + ("topk_device.hpp", "topk_internal.hpp", "topk_cols_api.cpp")
     h = hashlib.sha256()
     for p in sorted(p for p in B.SOURCES + B.HEADERS if os.path.basename(p) in names):
         with open(p, "rb") as f:

@@ -101,6 +101,12 @@ int topk_cols_create(topk_cols_t *out, int64_t V, int64_t C, int32_t k, int32_t 
  * ordered on a single stream: the workspace serves one run at a time.  Use a
  * separate handle for each stream that runs concurrently.
  *
+ * Graph capture: a row-interleaved run leaves the workspace as it found it
+ * (its second kernel clears what the first one shared), so it may be
+ * captured and replayed.  A column-contiguous run tags its keys with a value
+ * chosen on the host for each call; a replay would repeat the tag, so those
+ * runs must not be captured.
+ *
  * Returns TOPK_ERR_INVALID_ARG for a NULL or misaligned pointer, or a NULL
  * handle.  Returns TOPK_ERR_HIP when the launch fails.
  */
