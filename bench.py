@@ -24,7 +24,9 @@ The script prints one JSON line on stdout.  Progress goes to stderr.
                        kernel source changed after the counters were taken.
   per_config           the same measurements for all five workloads, with the
                        launch floor of an empty kernel and the warm-cache
-                       figure.
+                       figure; for the column-contiguous workloads also the
+                       one-wave-per-column baseline kernel (the design the
+                       page replaced) under the same protocol.
   cpu_baseline         the CPU oracle timed on this host's cores on whole
                        rounds of the headline workload.
 """
@@ -90,11 +92,11 @@ class Rotation:
         torch.cuda.synchronize()
 
 
-def time_config(torch, T, w, steps, warmup, per_call_steps=None, warm=True):
+def time_config(torch, T, w, steps, warmup, per_call_steps=None, warm=True, algo="auto"):
     """Amortized and per-call timings of one workload (cold HBM by rotation)."""
     import numpy as np
     rot = Rotation(torch, w)
-    h = T.TopkCols(w.V, w.C, w.k, w.dtype, w.layout, w.ld)
+    h = T.TopkCols(w.V, w.C, w.k, w.dtype, w.layout, w.ld, algo=algo)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     vals = torch.empty((w.C, w.k), dtype=rot.buf.dtype, device="cuda")
@@ -317,6 +319,8 @@ def main():
     ap.add_argument("--configs", default="1,2,3,4,5",
                     help="workloads measured for per_config (the headline is always measured)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-one-wave", action="store_true",
+                    help="skip timing the one-wave-per-column baseline kernel")
     ap.add_argument("--profile", type=int, nargs="?", const=HEADLINE, default=None, metavar="N",
                     help="profiling run: workload N only (default: the headline), few steps, "
                          "plus a plain copy of known size")
@@ -401,6 +405,18 @@ def main():
         log(f"  {r['us_per_round']:.2f} us/round (per call {r['per_call_median_us']:.2f} us, "
             f"warm {r.get('warm_us_per_round', float('nan')):.2f} us, host {r['host_enqueue_us_per_call']:.2f} us), "
             f"{r['gbps']:.0f} GB/s = {100 * r['frac_of_peak']:.1f}% of peak, exact={exact}")
+        if w.layout == "col" and not args.no_one_wave:
+            # the design the pages replaced (one wave per column), same protocol
+            rb = time_config(torch, T, w, 100, 10, per_call_steps=50, warm=False, algo="one_wave")
+            bv, bi = rb.pop("_last")
+            r["one_wave_baseline"] = {
+                "us_per_round": rb["us_per_round"],
+                "per_call_median_us": rb["per_call_median_us"],
+                "speedup_of_split_kernel": rb["us_per_round"] / r["us_per_round"],
+                "bit_exact_vs_oracle": bool(np.array_equal(bi, oi) and np.array_equal(bv.view(st), ov.view(st))),
+            }
+            log(f"  one wave per column: {rb['us_per_round']:.2f} us/round "
+                f"({rb['us_per_round'] / r['us_per_round']:.1f}x the split kernel)")
         if n == HEADLINE:
             headline = (w, r)
 

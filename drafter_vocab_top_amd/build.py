@@ -14,7 +14,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libtopk_cols.so")
-SOURCES = [os.path.join(CSRC, n) for n in ("topk_col.hip", "topk_colw.hip", "topk_row.hip", "topk_cols_api.cpp")]
+SOURCES = [os.path.join(CSRC, n) for n in ("topk_col.hip", "topk_colw.hip", "topk_row.hip", "topk_onewave.hip",
+                                            "topk_cols_api.cpp")]
+OBJDIR = os.path.join(ROOT, "_build")
 HEADERS = [os.path.join(CSRC, n) for n in ("topk_device.hpp", "topk_col_common.hpp", "topk_internal.hpp")] + \
           [os.path.join(INCLUDE, "topk_cols.h")]
 ARCH = "gfx950"
@@ -26,26 +28,46 @@ def hipcc():
     return path if os.path.exists(path) else "hipcc"
 
 
-def command(output=LIBRARY):
-    return [hipcc(), "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
+def flags():
+    return ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
             # keep the compiler from emitting packed fp32 instructions
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wall", "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC,
-            "-o", output] + SOURCES
+            "-Wall", "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC]
 
 
-def build(verbose=False):
-    tmp = LIBRARY + ".tmp"
-    cmd = command(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+def command(output=LIBRARY):
+    """One hipcc line that builds the whole library (for reference)."""
+    return [hipcc()] + flags() + ["-shared", "-o", output] + SOURCES
+
+
+def _check(res, what, verbose):
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+        raise RuntimeError(f"hipcc failed on {what} ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+
+
+def build(verbose=False):
+    """Compiles every source to an object in parallel, then links the library."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
+        cmd = [hipcc()] + flags() + ["-c", "-o", obj, src]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+        objs.append(obj)
+    for src, pr in procs:
+        out, err = pr.communicate()
+        _check(subprocess.CompletedProcess(pr.args, pr.returncode, out, err), os.path.basename(src), verbose)
+    tmp = LIBRARY + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    _check(subprocess.run(cmd, capture_output=True, text=True), "link", verbose)
     os.replace(tmp, LIBRARY)
     return LIBRARY
 

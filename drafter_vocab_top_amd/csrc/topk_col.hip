@@ -471,7 +471,7 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
         static_cast<storage*>(a.out_values)[(int64_t)c * k + pos] =
             (storage)((o == DT::kZeroOrder || o == DT::kNanOrder) ? (uint32_t)col[row]
                                                                   : DT::bits_from_order(o));
-        a.out_ids[(int64_t)c * k + pos] = (int32_t)row;
+        a.out_ids[(int64_t)c * k + pos] = a.id_map ? a.id_map[row] : (int32_t)row;
     };
     if ((uint32_t)a.S * k <= (uint32_t)kWaveMergeKeys) {
         if (wave != 0) return;

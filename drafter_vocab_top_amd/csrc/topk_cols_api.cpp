@@ -26,6 +26,7 @@ struct topk_cols {
     uint64_t* partials;
     uint32_t* bound;    // row layout: per-column lower bounds shared by the segments
     uint32_t runs;      // completed run() calls, for the run tag
+    uint8_t* col_tag;   // column layout: the tag of the last run that wrote each column's lists
 };
 
 namespace {
@@ -120,7 +121,9 @@ int create_impl(topk_cols_t* out, int64_t V, int64_t C, int32_t k, int32_t dtype
     if (layout == TOPK_COL_CONTIG && ld < V) return TOPK_ERR_INVALID_ARG;
     if (layout == TOPK_ROW_INTERLEAVED && ld < C) return TOPK_ERR_INVALID_ARG;
     if (forced_segments < 0) return TOPK_ERR_INVALID_ARG;
-    if (algo != TOPK_ALGO_AUTO && algo != TOPK_ALGO_WORKGROUP && algo != TOPK_ALGO_WAVE) return TOPK_ERR_INVALID_ARG;
+    if (algo != TOPK_ALGO_AUTO && algo != TOPK_ALGO_WORKGROUP && algo != TOPK_ALGO_WAVE &&
+        algo != TOPK_ALGO_ONE_WAVE)
+        return TOPK_ERR_INVALID_ARG;
     if (k > TOPK_MAX_K || V > TOPK_MAX_V) return TOPK_ERR_UNSUPPORTED;
     const bool row = layout == TOPK_ROW_INTERLEAVED;
     if (!row && forced_segments > topk::kMaxSegments) return TOPK_ERR_UNSUPPORTED;
@@ -128,6 +131,8 @@ int create_impl(topk_cols_t* out, int64_t V, int64_t C, int32_t k, int32_t dtype
     if (row && forced_segments * k > topk::kRowMaxMergeKeys) return TOPK_ERR_UNSUPPORTED;
     if (!row && algo == TOPK_ALGO_WAVE && forced_segments > 0 && !wave_fits(forced_segments, k))
         return TOPK_ERR_UNSUPPORTED;
+    if (algo == TOPK_ALGO_ONE_WAVE && forced_segments > 1) return TOPK_ERR_UNSUPPORTED;  // no split
+    if (C > 0x7FFFFFFF) return TOPK_ERR_UNSUPPORTED;
 
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess) return TOPK_ERR_HIP;
@@ -142,8 +147,10 @@ int create_impl(topk_cols_t* out, int64_t V, int64_t C, int32_t k, int32_t dtype
             algo = TOPK_ALGO_WORKGROUP;
     }
     const bool wave = !row && algo == TOPK_ALGO_WAVE;
+    const bool one_wave = !row && algo == TOPK_ALGO_ONE_WAVE;
     const int64_t tiles = row ? ceil_div(C, topk::row_tile_columns(dtype)) : 0;
-    const int64_t S = forced_segments > 0 ? forced_segments
+    const int64_t S = one_wave ? 1
+                      : forced_segments > 0 ? forced_segments
                       : row  ? choose_row_segments(V, tiles, k, cu_count)
                       : wave ? choose_wave_segments(V, C, dtype, k, cu_count)
                              : choose_col_segments(V, C, dtype, cu_count);
@@ -159,6 +166,14 @@ int create_impl(topk_cols_t* out, int64_t V, int64_t C, int32_t k, int32_t dtype
 
     topk_cols* h = new (std::nothrow) topk_cols();
     if (!h) return TOPK_ERR_OUT_OF_MEMORY;
+    h->col_tag = nullptr;
+    if (!row) {
+        h->col_tag = new (std::nothrow) uint8_t[(size_t)C]();  // 0: never written (no run uses tag 0)
+        if (!h->col_tag) {
+            delete h;
+            return TOPK_ERR_OUT_OF_MEMORY;
+        }
+    }
     h->V = V; h->C = C; h->ld = ld; h->k = k; h->dtype = dtype; h->layout = layout;
     h->device = device; h->segments = S; h->blocks = blocks; h->tiles = tiles;
     h->algo = row ? (int32_t)TOPK_ALGO_AUTO : algo;
@@ -167,6 +182,7 @@ int create_impl(topk_cols_t* out, int64_t V, int64_t C, int32_t k, int32_t dtype
     hipError_t e = hipMalloc(&h->workspace, ws_bytes);
     if (e != hipSuccess) {
         (void)hipGetLastError();
+        delete[] h->col_tag;
         delete h;
         return e == hipErrorOutOfMemory ? TOPK_ERR_OUT_OF_MEMORY : TOPK_ERR_HIP;
     }
@@ -175,6 +191,7 @@ int create_impl(topk_cols_t* out, int64_t V, int64_t C, int32_t k, int32_t dtype
     h->bound = row ? reinterpret_cast<uint32_t*>(static_cast<char*>(h->workspace) + ticket_bytes + list_bytes) : nullptr;
     if (hipMemset(h->workspace, 0, ws_bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
         (void)hipFree(h->workspace);
+        delete[] h->col_tag;
         delete h;
         return TOPK_ERR_HIP;
     }
@@ -201,13 +218,36 @@ int topk_cols_create_tuned(topk_cols_t* out, int64_t V, int64_t C, int32_t k, in
     return create_impl(out, V, C, k, dtype, layout, ld, segments, algo);
 }
 
-int topk_cols_run(topk_cols_t h, const void* logits, void* out_values, int32_t* out_ids,
-                  hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The run tag for the column layout: the first value in 1..255, starting
+// from the handle's run count, that no active column's lists carry from an
+// earlier run.  The last workgroup of a column tells a list slot written in
+// this run from a stale one by its tag, so a column must never see its own
+// previous tag again while its old lists are still there; with runs over
+// fewer columns, a column's last write can be any number of runs back.
+// Returns 0 when every tag is taken (then the caller clears the lists).
+uint32_t choose_tag(const topk_cols* h, int64_t n) {
+    uint64_t used[4] = {0, 0, 0, 0};
+    for (int64_t c = 0; c < n; ++c) used[h->col_tag[c] >> 6] |= 1ull << (h->col_tag[c] & 63u);
+    for (uint32_t i = 0; i < 255u; ++i) {
+        const uint32_t t = 1u + ((h->runs + i) % 255u);
+        if (!((used[t >> 6] >> (t & 63u)) & 1ull)) return t;
+    }
+    return 0;
+}
+
+int run_impl(topk_cols_t h, int64_t n_cols, const void* logits, const int32_t* id_map,
+             void* out_values, int32_t* out_ids, hipStream_t stream) {
     if (!h || !logits || !out_values || !out_ids) return TOPK_ERR_INVALID_ARG;
+    if (n_cols < 0 || n_cols > h->C) return TOPK_ERR_INVALID_ARG;
     const uintptr_t es = (uintptr_t)element_size(h->dtype);
     if (((uintptr_t)logits % es) != 0 || ((uintptr_t)out_values % es) != 0 ||
-        ((uintptr_t)out_ids % 4) != 0)
+        ((uintptr_t)out_ids % 4) != 0 || ((uintptr_t)id_map % 4) != 0)
         return TOPK_ERR_INVALID_ARG;
+    if (n_cols == 0) return TOPK_OK;
 
     hipError_t e;
     if (h->layout == TOPK_ROW_INTERLEAVED) {
@@ -215,10 +255,10 @@ int topk_cols_run(topk_cols_t h, const void* logits, void* out_values, int32_t* 
         a.x = logits;
         a.ld = h->ld;
         a.V = h->V;
-        a.C = (int32_t)h->C;
+        a.C = (int32_t)n_cols;
         a.k = h->k;
         a.S = (int32_t)h->segments;
-        a.tiles = (int32_t)h->tiles;
+        a.tiles = (int32_t)ceil_div(n_cols, topk::row_tile_columns(h->dtype));
         a.vec_loads = ((uintptr_t)logits % 16 == 0 && (h->ld * (int64_t)es) % 16 == 0) ? 1 : 0;
         a.key32 = (h->dtype == TOPK_BF16 && ceil_div(h->V, h->segments) <= 65536) ? 1 : 0;
         a.partials = h->partials;
@@ -226,32 +266,72 @@ int topk_cols_run(topk_cols_t h, const void* logits, void* out_values, int32_t* 
         a.use_bound = h->k <= topk::kRowBoundSlots ? 1 : 0;
         a.out_values = out_values;
         a.out_ids = out_ids;
+        a.id_map = id_map;
         e = topk::launch_row(h->dtype, h->nv, a, stream);
     } else {
         topk::ColArgs a;
         a.x = logits;
         a.ld = h->ld;
         a.V = h->V;
-        a.C = (int32_t)h->C;
+        a.C = (int32_t)n_cols;
         a.k = h->k;
         a.S = (int32_t)h->segments;
-        a.tag = 1u + (h->runs % 255u);
         a.partials = h->partials;
         a.tickets = h->tickets;
         a.out_values = out_values;
         a.out_ids = out_ids;
-        e = h->algo == TOPK_ALGO_WAVE ? topk::launch_colw(h->dtype, h->nv, a, stream)
-                                      : topk::launch_col(h->dtype, h->nv, a, stream);
+        a.id_map = id_map;
+        if (h->algo == TOPK_ALGO_ONE_WAVE) {
+            a.tag = 0;
+            e = topk::launch_onewave(h->dtype, a, stream);
+        } else {
+            uint32_t tag = choose_tag(h, n_cols);
+            if (tag == 0) {
+                // every tag is still held by some active column's lists: clear
+                // them all (tag 0 is never a run's tag)
+                const size_t list_bytes = (size_t)h->workspace_bytes -
+                                          (size_t)((char*)h->partials - (char*)h->workspace);
+                if (hipMemsetAsync(h->partials, 0, list_bytes, stream) != hipSuccess) return TOPK_ERR_HIP;
+                for (int64_t c = 0; c < h->C; ++c) h->col_tag[c] = 0;
+                tag = 1u + (h->runs % 255u);
+            }
+            a.tag = tag;
+            e = h->algo == TOPK_ALGO_WAVE ? topk::launch_colw(h->dtype, h->nv, a, stream)
+                                          : topk::launch_col(h->dtype, h->nv, a, stream);
+            if (e == hipSuccess)
+                for (int64_t c = 0; c < n_cols; ++c) h->col_tag[c] = (uint8_t)tag;
+        }
     }
     if (e != hipSuccess) return TOPK_ERR_HIP;
     ++h->runs;
     return TOPK_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int topk_cols_run(topk_cols_t h, const void* logits, void* out_values, int32_t* out_ids,
+                  hipStream_t stream) {
+    return run_impl(h, h ? h->C : 0, logits, nullptr, out_values, out_ids, stream);
+}
+
+int topk_cols_run_n(topk_cols_t h, int64_t n_cols, const void* logits, void* out_values,
+                    int32_t* out_ids, hipStream_t stream) {
+    return run_impl(h, n_cols, logits, nullptr, out_values, out_ids, stream);
+}
+
+int topk_cols_run_mapped(topk_cols_t h, int64_t n_cols, const void* logits, const int32_t* row_to_id,
+                         void* out_values, int32_t* out_ids, hipStream_t stream) {
+    if (!row_to_id) return TOPK_ERR_INVALID_ARG;
+    return run_impl(h, n_cols, logits, row_to_id, out_values, out_ids, stream);
+}
+
 int topk_cols_destroy(topk_cols_t h) {
     if (!h) return TOPK_OK;
     int status = TOPK_OK;
     if (h->workspace && hipFree(h->workspace) != hipSuccess) status = TOPK_ERR_HIP;
+    delete[] h->col_tag;
     delete h;
     return status;
 }

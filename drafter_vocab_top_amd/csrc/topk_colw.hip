@@ -259,7 +259,7 @@ __global__ __launch_bounds__(kBlock) void topk_colw_kernel(ColArgs a) {
         const uint32_t row = key_row(key), o = key_order(key);
         static_cast<storage*>(a.out_values)[(int64_t)c * k + lane] =
             (storage)((o == DT::kZeroOrder || o == DT::kNanOrder) ? (uint32_t)col[row] : DT::bits_from_order(o));
-        a.out_ids[(int64_t)c * k + lane] = (int32_t)row;
+        a.out_ids[(int64_t)c * k + lane] = a.id_map ? a.id_map[row] : (int32_t)row;
     }
     if (lane == 0)
         __hip_atomic_store(&a.tickets[c * kTicketStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

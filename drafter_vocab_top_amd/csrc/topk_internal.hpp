@@ -23,6 +23,7 @@ struct ColArgs {
     uint32_t* tickets;    // C counters kTicketStride apart, zero between runs
     void* out_values;     // C*k elements of the input dtype
     int32_t* out_ids;     // C*k
+    const int32_t* id_map;  // NULL, or V entries: out_ids holds id_map[row] instead of row
 };
 
 // Waves per workgroup of the column-contiguous kernel.
@@ -45,6 +46,11 @@ hipError_t launch_col(int dtype, int nv, const ColArgs& a, hipStream_t stream);
 constexpr int kWaveSegMergeKeys = 2048;
 hipError_t launch_colw(int dtype, int nv, const ColArgs& a, hipStream_t stream);
 
+// Column-contiguous, one wave per column and no vocabulary split (the
+// baseline design): C workgroups of 64 lanes; S, tag, partials and tickets
+// are not used.
+hipError_t launch_onewave(int dtype, const ColArgs& a, hipStream_t stream);
+
 // Row-interleaved launch: element (r, c) at x[r*ld + c].  The scan grid is
 // tiles*S workgroups: workgroup b handles row segment b / tiles and column
 // tile b % tiles (128 bytes of each row); a second kernel merges each
@@ -64,6 +70,7 @@ struct RowArgs {
     int32_t use_bound;    // 1 if k <= kRowBoundSlots: segments share a lower bound per column
     void* out_values;     // C*k elements of the input dtype
     int32_t* out_ids;     // C*k
+    const int32_t* id_map;  // NULL, or V entries: out_ids holds id_map[row] instead of row
 };
 
 constexpr int kRowMaxMergeKeys = 2048;

@@ -874,7 +874,7 @@ __global__ __launch_bounds__(kBlock) void topk_row_merge(RowArgs a) {
         static_cast<storage*>(a.out_values)[(int64_t)col * k + lane] =
             (storage)((o == DT::kZeroOrder || o == DT::kNanOrder) ? (uint32_t)x[(int64_t)row * a.ld + col]
                                                                   : DT::bits_from_order(o));
-        a.out_ids[(int64_t)col * k + lane] = (int32_t)row;
+        a.out_ids[(int64_t)col * k + lane] = a.id_map ? a.id_map[row] : (int32_t)row;
     }
 }
 

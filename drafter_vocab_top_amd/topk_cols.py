@@ -31,9 +31,11 @@ DTYPES = {"bf16": 0, "f32": 1}
 LAYOUTS = {"col": 0, "row": 1}
 
 EXPORTED = ("topk_cols_create", "topk_cols_create_with_segments", "topk_cols_create_tuned",
-            "topk_cols_run", "topk_cols_destroy", "topk_cols_status_string", "topk_cols_query")
-# kernel families of the column-contiguous layout
-ALGOS = {"auto": 0, "workgroup": 1, "wave": 2}
+            "topk_cols_run", "topk_cols_run_n", "topk_cols_run_mapped", "topk_cols_destroy",
+            "topk_cols_status_string", "topk_cols_query")
+# kernel families of the column-contiguous layout ("one_wave": the baseline
+# design with one wave per column and no vocabulary split)
+ALGOS = {"auto": 0, "workgroup": 1, "wave": 2, "one_wave": 3}
 
 _lib = None
 
@@ -61,6 +63,10 @@ def load(path: str = LIBRARY):
     lib.topk_cols_create_tuned.restype = ctypes.c_int
     lib.topk_cols_run.argtypes = [p, p, p, p, p]
     lib.topk_cols_run.restype = ctypes.c_int
+    lib.topk_cols_run_n.argtypes = [p, i64, p, p, p, p]
+    lib.topk_cols_run_n.restype = ctypes.c_int
+    lib.topk_cols_run_mapped.argtypes = [p, i64, p, p, p, p, p]
+    lib.topk_cols_run_mapped.restype = ctypes.c_int
     lib.topk_cols_destroy.argtypes = [p]
     lib.topk_cols_destroy.restype = ctypes.c_int
     lib.topk_cols_status_string.argtypes = [ctypes.c_int]
@@ -106,19 +112,38 @@ class TopkCols:
         names = {v: n for n, v in ALGOS.items()}
         return {"segments": s.value, "blocks": b.value, "workspace_bytes": w.value, "algo": names.get(a.value)}
 
-    def run_ptr(self, x_ptr: int, values_ptr: int, ids_ptr: int, stream_ptr: int) -> None:
-        """Enqueue one run on raw device pointers and a raw HIP stream handle."""
-        rc = load().topk_cols_run(self._h, x_ptr, values_ptr, ids_ptr, stream_ptr)
-        if rc != TOPK_OK:
-            raise TopkError(rc, "topk_cols_run")
+    def run_ptr(self, x_ptr: int, values_ptr: int, ids_ptr: int, stream_ptr: int,
+                n_cols: int | None = None, id_map_ptr: int | None = None) -> None:
+        """Enqueue one run on raw device pointers and a raw HIP stream handle.
 
-    def run(self, x, values=None, ids=None, stream=None):
+        n_cols: active columns (topk_cols_run_n); None runs all C columns.
+        id_map_ptr: device row -> id table (topk_cols_run_mapped), or None.
+        """
+        lib = load()
+        if id_map_ptr is not None:
+            rc = lib.topk_cols_run_mapped(self._h, self.C if n_cols is None else n_cols, x_ptr, id_map_ptr,
+                                          values_ptr, ids_ptr, stream_ptr)
+            what = "topk_cols_run_mapped"
+        elif n_cols is not None:
+            rc = lib.topk_cols_run_n(self._h, n_cols, x_ptr, values_ptr, ids_ptr, stream_ptr)
+            what = "topk_cols_run_n"
+        else:
+            rc = lib.topk_cols_run(self._h, x_ptr, values_ptr, ids_ptr, stream_ptr)
+            what = "topk_cols_run"
+        if rc != TOPK_OK:
+            raise TopkError(rc, what)
+
+    def run(self, x, values=None, ids=None, stream=None, n_cols: int | None = None, id_map=None):
         """Enqueue one run on torch tensors (on the current stream by default).
 
         x: GPU tensor holding the matrix (bf16 or fp32, or int16/uint16/int32
            bit patterns of the same width), laid out as given at creation.
         values/ids: optional preallocated outputs (C*k elements each).
-        Returns (values, ids) shaped (C, k).
+        n_cols: select over the first n_cols columns only (None: all C).
+        id_map: optional int32 GPU tensor of V entries; the ids returned are
+           id_map[row] (selection and tie order are unchanged).
+        Returns (values, ids) shaped (C, k); with n_cols, rows n_cols.. of
+        freshly allocated outputs are left uninitialised.
         """
         import torch
         if not x.is_cuda:
@@ -134,8 +159,14 @@ class TopkCols:
             ids = torch.empty((self.C, self.k), dtype=torch.int32, device=x.device)
         if values.numel() < self.C * self.k or ids.numel() < self.C * self.k:
             raise ValueError("output buffers are too small")
+        map_ptr = None
+        if id_map is not None:
+            if not id_map.is_cuda or id_map.dtype != torch.int32 or id_map.numel() < self.V \
+                    or not id_map.is_contiguous():
+                raise ValueError("id_map must be a contiguous int32 GPU tensor of V entries")
+            map_ptr = id_map.data_ptr()
         s = stream if stream is not None else torch.cuda.current_stream(x.device)
-        self.run_ptr(x.data_ptr(), values.data_ptr(), ids.data_ptr(), s.cuda_stream)
+        self.run_ptr(x.data_ptr(), values.data_ptr(), ids.data_ptr(), s.cuda_stream, n_cols, map_ptr)
         return values, ids
 
     def close(self) -> None:

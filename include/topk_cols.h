@@ -117,6 +117,48 @@ int topk_cols_run(topk_cols_t h, const void *logits, void *out_values, int32_t *
  * The caller must ensure no run on the handle is still in flight. */
 int topk_cols_destroy(topk_cols_t h);
 
+/*
+ * Like topk_cols_run, over the first n_cols columns only (0 <= n_cols <= C):
+ * a round in which fewer drafts are active than the handle was created for
+ * (the "DFlash2" page, "How it works": the drafter proposes up to
+ * spec.draft_tokens tokens per lane, so a round may carry fewer columns).
+ * Lay the active columns out first; with a per-lane draft count, pack each
+ * lane's active columns one after another and pass their total.
+ *
+ * Columns n_cols..C-1 of the matrix are not read, and out_values/out_ids are
+ * written only in their first n_cols*k entries (same layout as
+ * topk_cols_run).  n_cols = 0 enqueues nothing and returns TOPK_OK.  The
+ * handle's launch decomposition (segments per column) stays the one chosen
+ * at create, and the results are the same as a run on a matrix of n_cols
+ * columns.  Ownership, ordering and capture rules are those of topk_cols_run.
+ * A column-contiguous run over fewer columns than the last may clear the
+ * handle's lists with hipMemsetAsync on the stream (when all 255 run tags
+ * are still held by some column's old lists).
+ *
+ * Returns TOPK_ERR_INVALID_ARG for n_cols < 0 or n_cols > C, and otherwise
+ * as topk_cols_run.
+ */
+int topk_cols_run_n(topk_cols_t h, int64_t n_cols, const void *logits, void *out_values,
+                    int32_t *out_ids, hipStream_t stream);
+
+/*
+ * Like topk_cols_run_n, with the row ids translated through a table: the
+ * "DFlash2" page ("How it works") describes a "shortlist" head that scores
+ * only the 131,072 most frequent tokens, so its row r stands for vocabulary
+ * token row_to_id[r].  Selection is unchanged: values compare as for
+ * topk_cols_run and ties go to the smaller ROW (shortlist position), not to
+ * the smaller token id.  Only the reported id changes:
+ * out_ids[c*k + j] = row_to_id[row of the j-th largest of column c].
+ *
+ * row_to_id: device, V int32 entries, 4-byte aligned, read-only, owned by
+ *            the caller; any values (the table need not be a permutation).
+ *
+ * Returns TOPK_ERR_INVALID_ARG for a NULL or misaligned row_to_id, and
+ * otherwise as topk_cols_run_n.
+ */
+int topk_cols_run_mapped(topk_cols_t h, int64_t n_cols, const void *logits, const int32_t *row_to_id,
+                         void *out_values, int32_t *out_ids, hipStream_t stream);
+
 /* A static, human-readable name for a status code.  Never NULL. */
 const char *topk_cols_status_string(int status);
 
@@ -136,7 +178,10 @@ int topk_cols_create_with_segments(topk_cols_t *out, int64_t V, int64_t C, int32
 typedef enum {
     TOPK_ALGO_AUTO = 0,       /* chosen from the shape */
     TOPK_ALGO_WORKGROUP = 1,  /* a workgroup per vocabulary segment */
-    TOPK_ALGO_WAVE = 2        /* a wave per vocabulary segment (4 per workgroup) */
+    TOPK_ALGO_WAVE = 2,       /* a wave per vocabulary segment (4 per workgroup) */
+    TOPK_ALGO_ONE_WAVE = 3    /* one wave per column and no vocabulary split: the design that the
+                                 "DFlash2" page ("How it works") replaced, kept as a baseline;
+                                 never chosen automatically */
 } topk_algo;
 
 /*
@@ -144,7 +189,8 @@ typedef enum {
  * (column-contiguous layout; the row-interleaved layout accepts only
  * TOPK_ALGO_AUTO).  For tests and tuning: every family gives the same result.
  * With TOPK_ALGO_WAVE, 4 * segments * k above 2048 returns
- * TOPK_ERR_UNSUPPORTED.  An unknown algo returns TOPK_ERR_INVALID_ARG.
+ * TOPK_ERR_UNSUPPORTED.  TOPK_ALGO_ONE_WAVE accepts segments 0 or 1 only
+ * (else TOPK_ERR_UNSUPPORTED).  An unknown algo returns TOPK_ERR_INVALID_ARG.
  */
 int topk_cols_create_tuned(topk_cols_t *out, int64_t V, int64_t C, int32_t k, int32_t dtype,
                            int32_t layout, int64_t ld, int64_t segments, int32_t algo);

@@ -69,3 +69,20 @@ def topk_cols(x, V, C, k, dtype, layout, ld, nthreads=1, lib=None):
     if rc != 0:
         raise ValueError(f"oracle_topk_cols failed with status {rc}")
     return values, ids
+
+
+def topk_cols_mapped(x, V, C, k, dtype, layout, ld, row_to_id, nthreads=1, lib=None):
+    """Top-k of every column with the row ids translated through a table.
+
+    The "DFlash2" page ("How it works") describes a "shortlist" output head
+    that scores only the 131,072 most frequent vocabulary tokens, so the
+    head's row r stands for token row_to_id[r].  Reading taken: the selection
+    is the one of topk_cols -- larger value first, ties to the smaller ROW
+    (shortlist position) -- and only the reported id is translated afterwards.
+    Returns (values, row_to_id[ids]).
+    """
+    row_to_id = np.asarray(row_to_id)
+    if row_to_id.shape != (V,):
+        raise ValueError("row_to_id must hold one id per row")
+    values, ids = topk_cols(x, V, C, k, dtype, layout, ld, nthreads=nthreads, lib=lib)
+    return values, row_to_id[ids].astype(np.int32)

@@ -94,8 +94,12 @@ def test_tuned_create_checks_its_arguments(lib):
         h = ctypes.c_void_p(0xDEAD)
         rc = lib.topk_cols_create_tuned(ctypes.byref(h), *args)
         return rc, h
-    rc, h = tuned(100, 7, 8, 0, 0, 100, 0, 3)           # unknown algorithm
+    rc, h = tuned(100, 7, 8, 0, 0, 100, 0, 4)           # unknown algorithm
     assert rc == T.TOPK_ERR_INVALID_ARG and h.value is None
+    rc, h = tuned(100, 7, 8, 0, 0, 100, 2, 3)           # one wave per column: no split
+    assert rc == T.TOPK_ERR_UNSUPPORTED and h.value is None
+    rc, h = tuned(100, 448, 8, 0, 1, 448, 0, 3)         # ... and column-contiguous only
+    assert rc == T.TOPK_ERR_UNSUPPORTED and h.value is None
     rc, h = tuned(100, 448, 8, 0, 1, 448, 0, 2)         # row-interleaved takes only "auto"
     assert rc == T.TOPK_ERR_UNSUPPORTED and h.value is None
     rc, h = tuned(100000, 56, 64, 0, 0, 100000, 9, 2)   # wave merge: 4*9*64 > 2048 keys
@@ -109,6 +113,8 @@ def test_null_out_pointer_refused(lib):
 def test_null_handle_calls(lib):
     assert lib.topk_cols_destroy(None) == T.TOPK_OK
     assert lib.topk_cols_run(None, 16, 16, 16, None) == T.TOPK_ERR_INVALID_ARG
+    assert lib.topk_cols_run_n(None, 1, 16, 16, 16, None) == T.TOPK_ERR_INVALID_ARG
+    assert lib.topk_cols_run_mapped(None, 1, 16, 16, 16, 16, None) == T.TOPK_ERR_INVALID_ARG
     assert lib.topk_cols_query(None, None, None, None, None) == T.TOPK_ERR_INVALID_ARG
 
 
