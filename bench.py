@@ -26,7 +26,10 @@ The script prints one JSON line on stdout.  Progress goes to stderr.
                        launch floor of an empty kernel and the warm-cache
                        figure; for the column-contiguous workloads also the
                        one-wave-per-column baseline kernel (the design the
-                       page replaced) under the same protocol.
+                       page replaced) under the same protocol, and for all a
+                       plain streaming read of the same bytes
+                       (stream_read.hip) as the achievable-bandwidth
+                       reference.
   cpu_baseline         the CPU oracle timed on this host's cores on whole
                        rounds of the headline workload.
 """
@@ -88,6 +91,7 @@ class Rotation:
         for r in range(self.R):
             self.buf[r * per:r * per + n].copy_(src)
         self.ptrs = [self.buf[r * per:].data_ptr() for r in range(self.R)]
+        self.views = [self.buf[r * per:r * per + n] for r in range(self.R)]
         self.first = self.buf[:n]
         torch.cuda.synchronize()
 
@@ -161,6 +165,38 @@ def time_config(torch, T, w, steps, warmup, per_call_steps=None, warm=True, algo
     del rot
     torch.cuda.empty_cache()
     return res
+
+
+def stream_read_reference(torch, w, steps, warmup=20):
+    """Achievable-bandwidth reference: a plain streaming read of the same
+    bytes (drafter_vocab_top_amd/csrc/stream_read.hip, 16-byte non-temporal
+    loads, xor fold), same rotation over >= 1 GiB and event protocol as the
+    top-k.  Not part of the path."""
+    import ctypes
+    from drafter_vocab_top_amd import build as B
+    lib = ctypes.CDLL(B.STREAM_LIBRARY)
+    lib.stream_read_run.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.stream_read_run.restype = ctypes.c_int
+    rot = Rotation(torch, w)
+    # the matrix's bytes, rounded down to whole 16-byte vectors
+    nbytes = (rot.views[0].numel() * rot.views[0].element_size()) // 16 * 16
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp, sk = stream.cuda_stream, sink.data_ptr()
+    for s in range(warmup):
+        if lib.stream_read_run(rot.ptrs[s % rot.R], nbytes, sk, sp) != 0:
+            raise RuntimeError("stream_read_run failed")
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for s in range(steps):
+        lib.stream_read_run(rot.ptrs[s % rot.R], nbytes, sk, sp)
+    e1.record(stream)
+    e1.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / steps
+    del rot
+    torch.cuda.empty_cache()
+    return us, nbytes
 
 
 def launch_floor(torch, steps):
@@ -324,6 +360,8 @@ def main():
     ap.add_argument("--profile", type=int, nargs="?", const=HEADLINE, default=None, metavar="N",
                     help="profiling run: workload N only (default: the headline), few steps, "
                          "plus a plain copy of known size")
+    ap.add_argument("--algo", default="auto", choices=["auto", "workgroup", "wave", "one_wave"],
+                    help="kernel family for a --profile run (column-contiguous workloads)")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "N"),
                     help="turn the counter_collection.csv files of a FETCH_SIZE and a WRITE_SIZE "
                          "rocprofv3 run of '--profile N' into profiles/topk_*_cfgN_traffic.json")
@@ -352,7 +390,7 @@ def main():
 
     if args.profile is not None:
         w = W.config(args.profile)
-        res = time_config(torch, T, w, args.steps, args.warmup, warm=False)
+        res = time_config(torch, T, w, args.steps, args.warmup, warm=False, algo=args.algo)
         # a plain copy of known size, for scaling the traffic counters
         src = torch.empty(COPY_BYTES // 4, dtype=torch.int32, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -405,6 +443,15 @@ def main():
         log(f"  {r['us_per_round']:.2f} us/round (per call {r['per_call_median_us']:.2f} us, "
             f"warm {r.get('warm_us_per_round', float('nan')):.2f} us, host {r['host_enqueue_us_per_call']:.2f} us), "
             f"{r['gbps']:.0f} GB/s = {100 * r['frac_of_peak']:.1f}% of peak, exact={exact}")
+        try:
+            ref_us, ref_bytes = stream_read_reference(torch, w, 1000 if n != 5 else 200)
+            r["stream_read_reference"] = {
+                "us_per_round": ref_us, "bytes": ref_bytes, "gbps": ref_bytes / (ref_us * 1e3),
+                "topk_over_read_time": r["us_per_round"] / ref_us,
+                "kind": "plain streaming read of the same bytes (stream_read.hip; not part of the path)"}
+            log(f"  plain streaming read of the same bytes: {ref_us:.2f} us ({ref_bytes / (ref_us * 1e3):.0f} GB/s)")
+        except (RuntimeError, OSError) as e:
+            log(f"  plain read reference failed: {e}")
         if w.layout == "col" and not args.no_one_wave:
             # the design the pages replaced (one wave per column), same protocol
             rb = time_config(torch, T, w, 100, 10, per_call_steps=50, warm=False, algo="one_wave")

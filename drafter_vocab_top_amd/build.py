@@ -17,6 +17,10 @@ LIBRARY = os.path.join(HERE, "libtopk_cols.so")
 SOURCES = [os.path.join(CSRC, n) for n in ("topk_col.hip", "topk_colw.hip", "topk_row.hip", "topk_onewave.hip",
                                             "topk_cols_api.cpp")]
 OBJDIR = os.path.join(ROOT, "_build")
+# A plain streaming-read kernel that the benchmark times beside the top-k (not
+# part of the top-k library).
+STREAM_SOURCE = os.path.join(CSRC, "stream_read.hip")
+STREAM_LIBRARY = os.path.join(HERE, "libstream_read.so")
 HEADERS = [os.path.join(CSRC, n) for n in ("topk_device.hpp", "topk_col_common.hpp", "topk_internal.hpp")] + \
           [os.path.join(INCLUDE, "topk_cols.h")]
 ARCH = "gfx950"
@@ -53,7 +57,7 @@ def build(verbose=False):
     """Compiles every source to an object in parallel, then links the library."""
     os.makedirs(OBJDIR, exist_ok=True)
     objs, procs = [], []
-    for src in SOURCES:
+    for src in SOURCES + [STREAM_SOURCE]:
         obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
         cmd = [hipcc()] + flags() + ["-c", "-o", obj, src]
         if verbose:
@@ -63,12 +67,13 @@ def build(verbose=False):
     for src, pr in procs:
         out, err = pr.communicate()
         _check(subprocess.CompletedProcess(pr.args, pr.returncode, out, err), os.path.basename(src), verbose)
-    tmp = LIBRARY + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    _check(subprocess.run(cmd, capture_output=True, text=True), "link", verbose)
-    os.replace(tmp, LIBRARY)
+    for lib, lib_objs in ((LIBRARY, objs[:-1]), (STREAM_LIBRARY, objs[-1:])):
+        tmp = lib + ".tmp"
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + lib_objs
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        _check(subprocess.run(cmd, capture_output=True, text=True), "link", verbose)
+        os.replace(tmp, lib)
     return LIBRARY
 
 
