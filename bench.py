@@ -29,7 +29,8 @@ The script prints one JSON line on stdout.  Progress goes to stderr.
                        page replaced) under the same protocol, and for all a
                        plain streaming read of the same bytes
                        (stream_read.hip) as the achievable-bandwidth
-                       reference.
+                       reference, and the sampler that can follow the
+                       top-k (topk_cols_sample, T = 1, top_p = 0.95).
   cpu_baseline         the CPU oracle timed on this host's cores on whole
                        rounds of the headline workload.
 """
@@ -197,6 +198,31 @@ def stream_read_reference(torch, w, steps, warmup=20):
     del rot
     torch.cuda.empty_cache()
     return us, nbytes
+
+
+def time_sampler(torch, T, w, steps=1000, warmup=20):
+    """topk_cols_sample (T = 1.0, top_p = 0.95) on one run's top-k outputs,
+    back to back with the offset advanced per call; us per call."""
+    rot = Rotation(torch, w, copies=1)
+    with T.TopkCols(w.V, w.C, w.k, w.dtype, w.layout, w.ld) as h:
+        vals, ids = h.run(rot.first)
+        torch.cuda.synchronize()
+    out_ids = torch.empty(w.C, dtype=torch.int32, device="cuda")
+    out_pos = torch.empty(w.C, dtype=torch.int32, device="cuda")
+    lib, stream = T.load(), torch.cuda.current_stream()
+    sp, pv, pi, po, pp = stream.cuda_stream, vals.data_ptr(), ids.data_ptr(), out_ids.data_ptr(), out_pos.data_ptr()
+    dt = 0 if w.dtype == "bf16" else 1
+    for s in range(warmup):
+        lib.topk_cols_sample(pv, pi, w.C, w.k, dt, 1.0, 0.95, 7, s, po, pp, sp)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for s in range(steps):
+        lib.topk_cols_sample(pv, pi, w.C, w.k, dt, 1.0, 0.95, 7, s, po, pp, sp)
+    e1.record(stream)
+    e1.synchronize()
+    del rot
+    return e0.elapsed_time(e1) * 1000.0 / steps
 
 
 def launch_floor(torch, steps):
@@ -452,6 +478,8 @@ def main():
             log(f"  plain streaming read of the same bytes: {ref_us:.2f} us ({ref_bytes / (ref_us * 1e3):.0f} GB/s)")
         except (RuntimeError, OSError) as e:
             log(f"  plain read reference failed: {e}")
+        r["sampler_us_per_call"] = time_sampler(torch, T, w)
+        log(f"  sampling one draft per column (T=1, top_p=0.95): {r['sampler_us_per_call']:.2f} us")
         if w.layout == "col" and not args.no_one_wave:
             # the design the pages replaced (one wave per column), same protocol
             rb = time_config(torch, T, w, 100, 10, per_call_steps=50, warm=False, algo="one_wave")

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libtopk_cols.so")
 SOURCES = [os.path.join(CSRC, n) for n in ("topk_col.hip", "topk_colw.hip", "topk_row.hip", "topk_onewave.hip",
-                                            "topk_cols_api.cpp")]
+                                            "topk_sample.hip", "topk_cols_api.cpp")]
 OBJDIR = os.path.join(ROOT, "_build")
 # A plain streaming-read kernel that the benchmark times beside the top-k (not
 # part of the top-k library).

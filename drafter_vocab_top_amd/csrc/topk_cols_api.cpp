@@ -327,6 +327,33 @@ int topk_cols_run_mapped(topk_cols_t h, int64_t n_cols, const void* logits, cons
     return run_impl(h, n_cols, logits, row_to_id, out_values, out_ids, stream);
 }
 
+int topk_cols_sample(const void* values, const int32_t* ids, int64_t C, int32_t k, int32_t dtype,
+                     double temperature, double top_p, uint64_t seed, uint64_t offset, int32_t* out_ids,
+                     int32_t* out_pos, hipStream_t stream) {
+    if (!values || !ids || !out_ids) return TOPK_ERR_INVALID_ARG;
+    if (C < 1 || k < 1 || k > TOPK_MAX_K) return TOPK_ERR_INVALID_ARG;
+    if (dtype != TOPK_BF16 && dtype != TOPK_F32) return TOPK_ERR_INVALID_ARG;
+    if (!(temperature > 0.0) || temperature > 1.7976931348623157e308 || !(top_p > 0.0) || !(top_p <= 1.0))
+        return TOPK_ERR_INVALID_ARG;
+    const uintptr_t es = (uintptr_t)element_size(dtype);
+    if (((uintptr_t)values % es) != 0 || ((uintptr_t)ids % 4) != 0 || ((uintptr_t)out_ids % 4) != 0 ||
+        ((uintptr_t)out_pos % 4) != 0)
+        return TOPK_ERR_INVALID_ARG;
+    if ((C + 255) / 256 > 0x7FFFFFFF) return TOPK_ERR_UNSUPPORTED;
+    topk::SampleArgs a;
+    a.values = values;
+    a.ids = ids;
+    a.C = C;
+    a.k = k;
+    a.temperature = temperature;
+    a.top_p = top_p;
+    a.seed = seed;
+    a.offset = offset;
+    a.out_ids = out_ids;
+    a.out_pos = out_pos;
+    return topk::launch_sample(dtype, a, stream) == hipSuccess ? TOPK_OK : TOPK_ERR_HIP;
+}
+
 int topk_cols_destroy(topk_cols_t h) {
     if (!h) return TOPK_OK;
     int status = TOPK_OK;

@@ -76,6 +76,23 @@ struct RowArgs {
 constexpr int kRowMaxMergeKeys = 2048;
 constexpr int kRowBoundSlots = 16;
 
+// One sampled draft per column from its top-k list (values sorted largest
+// first, C*k of the dtype; ids C*k): out_ids[c] = ids[c*k + j*], out_pos[c] =
+// j* when out_pos is not NULL.
+struct SampleArgs {
+    const void* values;
+    const int32_t* ids;
+    int64_t C;
+    int32_t k;
+    double temperature;   // > 0, finite
+    double top_p;         // in (0, 1]
+    uint64_t seed;        // Philox key
+    uint64_t offset;      // Philox counter words 0-1 (the column is word 2)
+    int32_t* out_ids;
+    int32_t* out_pos;     // may be NULL
+};
+hipError_t launch_sample(int dtype, const SampleArgs& a, hipStream_t stream);
+
 // Columns per tile for a dtype (128 bytes of a row).
 int row_tile_columns(int dtype);
 hipError_t launch_row(int dtype, int nv, const RowArgs& a, hipStream_t stream);

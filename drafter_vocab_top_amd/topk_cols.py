@@ -31,8 +31,8 @@ DTYPES = {"bf16": 0, "f32": 1}
 LAYOUTS = {"col": 0, "row": 1}
 
 EXPORTED = ("topk_cols_create", "topk_cols_create_with_segments", "topk_cols_create_tuned",
-            "topk_cols_run", "topk_cols_run_n", "topk_cols_run_mapped", "topk_cols_destroy",
-            "topk_cols_status_string", "topk_cols_query")
+            "topk_cols_run", "topk_cols_run_n", "topk_cols_run_mapped", "topk_cols_sample",
+            "topk_cols_destroy", "topk_cols_status_string", "topk_cols_query")
 # kernel families of the column-contiguous layout ("one_wave": the baseline
 # design with one wave per column and no vocabulary split)
 ALGOS = {"auto": 0, "workgroup": 1, "wave": 2, "one_wave": 3}
@@ -67,6 +67,9 @@ def load(path: str = LIBRARY):
     lib.topk_cols_run_n.restype = ctypes.c_int
     lib.topk_cols_run_mapped.argtypes = [p, i64, p, p, p, p, p]
     lib.topk_cols_run_mapped.restype = ctypes.c_int
+    lib.topk_cols_sample.argtypes = [p, p, i64, i32, i32, ctypes.c_double, ctypes.c_double,
+                                     ctypes.c_uint64, ctypes.c_uint64, p, p, p]
+    lib.topk_cols_sample.restype = ctypes.c_int
     lib.topk_cols_destroy.argtypes = [p]
     lib.topk_cols_destroy.restype = ctypes.c_int
     lib.topk_cols_status_string.argtypes = [ctypes.c_int]
@@ -187,6 +190,34 @@ class TopkCols:
             self.close()
         except Exception:
             pass
+
+
+def sample(values, ids, temperature: float = 1.0, top_p: float = 0.95, seed: int = 0, offset: int = 0,
+           out_ids=None, out_pos=None, stream=None):
+    """One sampled draft per column from top-k outputs (topk_cols_sample).
+
+    values: (C, k) GPU tensor as a run wrote it (bf16 or fp32, or 16/32-bit
+    patterns); ids: (C, k) int32 GPU tensor.  Returns (ids, positions), each
+    (C,) int32 on the GPU; enqueued on the current stream by default.
+    """
+    import torch
+    if values.dim() != 2 or ids.shape != values.shape or ids.dtype != torch.int32:
+        raise ValueError("values and ids must be (C, k) tensors, ids int32")
+    if not (values.is_cuda and ids.is_cuda and values.is_contiguous() and ids.is_contiguous()):
+        raise ValueError("values and ids must be contiguous GPU tensors")
+    C, k = values.shape
+    dtype = 0 if values.element_size() == 2 else 1
+    if out_ids is None:
+        out_ids = torch.empty(C, dtype=torch.int32, device=values.device)
+    if out_pos is None:
+        out_pos = torch.empty(C, dtype=torch.int32, device=values.device)
+    s = stream if stream is not None else torch.cuda.current_stream(values.device)
+    rc = load().topk_cols_sample(values.data_ptr(), ids.data_ptr(), C, k, dtype, float(temperature),
+                                 float(top_p), int(seed), int(offset), out_ids.data_ptr(), out_pos.data_ptr(),
+                                 s.cuda_stream)
+    if rc != TOPK_OK:
+        raise TopkError(rc, "topk_cols_sample")
+    return out_ids, out_pos
 
 
 def topk_cols(x, V: int, C: int, k: int, dtype: str = "bf16", layout: str = "col", ld=None):

@@ -159,6 +159,43 @@ int topk_cols_run_n(topk_cols_t h, int64_t n_cols, const void *logits, void *out
 int topk_cols_run_mapped(topk_cols_t h, int64_t n_cols, const void *logits, const int32_t *row_to_id,
                          void *out_values, int32_t *out_ids, hipStream_t stream);
 
+/*
+ * Sample one draft per column from its top-k list (the step after the
+ * selection when the drafter samples: the "DFlash2" page measures sampled
+ * drafting at temperature 1.0, top_p 0.95 and top_k 20, section "Greedy
+ * coding is the best case" and the last row of "The numbers").  The page does
+ * not spell out the sampler; this is the standard reading.  For column c with
+ * top-k values v_0 >= ... >= v_{k-1} (values[c*k + j], largest first, as a
+ * topk_cols run writes them):
+ *   w_j = exp((v_j - v_0) / temperature),  S_m = w_0 + ... + w_{m-1},
+ *   n   = the smallest m with S_m >= top_p * S_k   (the nucleus),
+ *   u   = uniform in [0, 1) from Philox4x32-10 with counter
+ *         (offset & 0xFFFFFFFF, offset >> 32, c, 0) and key
+ *         (seed & 0xFFFFFFFF, seed >> 32): u = ((out0 << 32 | out1) >> 11) * 2^-53,
+ *   j*  = the smallest j < n with S_{j+1} > u * S_n,
+ * then out_ids[c] = ids[c*k + j*] and, if out_pos is not NULL,
+ * out_pos[c] = j*.  A column whose v_0 is not finite (NaN, +Inf, -Inf) takes
+ * j* = 0.  All arithmetic is IEEE double in the order written, with exp
+ * evaluated by a fixed method (Cody-Waite reduction, degree-13 Taylor
+ * polynomial by fused multiply-adds, ldexp), so the draw is reproducible
+ * bit for bit by any implementation of these steps.  The same (seed,
+ * offset, c) always gives the same u: advance offset between rounds.
+ *
+ * values: device, C*k elements of dtype (TOPK_BF16 or TOPK_F32), aligned to
+ *         the element size; each row sorted largest first.
+ * ids:    device, C*k int32 (rows, or token ids from topk_cols_run_mapped).
+ * out_ids: device, C int32.  out_pos: device, C int32, or NULL.
+ * All buffers are owned by the caller.  Asynchronous on stream; no
+ * allocation, no synchronization, no handle.
+ *
+ * Returns TOPK_ERR_INVALID_ARG for a NULL or misaligned pointer, C < 1,
+ * k < 1 or k > TOPK_MAX_K, an unknown dtype, temperature not finite and
+ * positive, or top_p outside (0, 1]; TOPK_ERR_HIP when the launch fails.
+ */
+int topk_cols_sample(const void *values, const int32_t *ids, int64_t C, int32_t k, int32_t dtype,
+                     double temperature, double top_p, uint64_t seed, uint64_t offset, int32_t *out_ids,
+                     int32_t *out_pos, hipStream_t stream);
+
 /* A static, human-readable name for a status code.  Never NULL. */
 const char *topk_cols_status_string(int status);
 

@@ -7,6 +7,8 @@ nothing from the GPU path.
 `topk_cols` wraps the plain-C oracle in topk_oracle.c (a full qsort of every
 column under the order "larger value first, ties to the smaller row id"; see
 that file's header for the readings of -0, NaN and the emitted bits).
+`sample_topk` wraps sample_oracle.c: one temperature / top-p draw per column
+from its top-k, with a Philox4x32-10 uniform (see that file's header).
 """
 import ctypes
 import os
@@ -30,6 +32,16 @@ def load_library(path):
     lib.oracle_topk_cols.argtypes = [
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int, ctypes.c_int,
         ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+    if not hasattr(lib, "oracle_sample_topk"):
+        return lib   # a planted-mistake build of topk_oracle.c alone
+    lib.oracle_sample_topk.restype = ctypes.c_int
+    lib.oracle_sample_topk.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int,
+        ctypes.c_double, ctypes.c_double, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.oracle_philox4x32_10.restype = None
+    lib.oracle_philox4x32_10.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.oracle_sample_exp.restype = ctypes.c_double
+    lib.oracle_sample_exp.argtypes = [ctypes.c_double]
     return lib
 
 
@@ -37,7 +49,8 @@ def _load():
     global _lib
     if _lib is None:
         path = _build.LIBRARY
-        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SOURCE):
+        if not os.path.exists(path) or any(os.path.getmtime(path) < os.path.getmtime(src)
+                                           for src in _build.SOURCES):
             _build.build()
         _lib = load_library(path)
     return _lib
@@ -86,3 +99,38 @@ def topk_cols_mapped(x, V, C, k, dtype, layout, ld, row_to_id, nthreads=1, lib=N
         raise ValueError("row_to_id must hold one id per row")
     values, ids = topk_cols(x, V, C, k, dtype, layout, ld, nthreads=nthreads, lib=lib)
     return values, row_to_id[ids].astype(np.int32)
+
+
+def sample_topk(values, ids, C, k, dtype, temperature, top_p, seed, offset, lib=None):
+    """One sampled draft per column from its top-k list (sample_oracle.c).
+
+    values: (C, k) stored bits (np.uint16 for bf16, np.uint32/np.float32 for
+    fp32), each row sorted largest first as the top-k path emits it; ids:
+    (C, k) int32.  Returns (sampled ids, positions in the list), int32 (C,).
+    """
+    values = np.ascontiguousarray(values)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    if values.size != C * k or ids.size != C * k:
+        raise ValueError("values and ids must hold C*k entries")
+    out_ids = np.empty(C, dtype=np.int32)
+    out_pos = np.empty(C, dtype=np.int32)
+    rc = (lib or _load()).oracle_sample_topk(values.ctypes.data, ids.ctypes.data, C, k, dtype,
+                                             float(temperature), float(top_p), int(seed), int(offset),
+                                             out_ids.ctypes.data, out_pos.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_sample_topk failed with status {rc}")
+    return out_ids, out_pos
+
+
+def philox4x32_10(counter, key):
+    """The oracle's Philox4x32-10 block: 4 counter words, 2 key words -> 4 words."""
+    c = np.asarray(counter, dtype=np.uint32)
+    kk = np.asarray(key, dtype=np.uint32)
+    out = np.empty(4, dtype=np.uint32)
+    _load().oracle_philox4x32_10(c.ctypes.data, kk.ctypes.data, out.ctypes.data)
+    return out
+
+
+def sample_exp(x):
+    """The oracle's fixed-method exp (x <= 0) used by sample_topk."""
+    return _load().oracle_sample_exp(float(x))

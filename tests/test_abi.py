@@ -115,6 +115,29 @@ def test_null_handle_calls(lib):
     assert lib.topk_cols_run(None, 16, 16, 16, None) == T.TOPK_ERR_INVALID_ARG
     assert lib.topk_cols_run_n(None, 1, 16, 16, 16, None) == T.TOPK_ERR_INVALID_ARG
     assert lib.topk_cols_run_mapped(None, 1, 16, 16, 16, 16, None) == T.TOPK_ERR_INVALID_ARG
+
+
+def test_sample_checks_its_arguments_before_any_launch(lib):
+    # pointers are never dereferenced on the host; every case fails validation
+    good = (16, 16, 4, 8, 1, 1.0, 0.95, 0, 0, 16, None, None)
+    def call(**kw):
+        a = list(good)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return lib.topk_cols_sample(*a)
+    assert call(a0=None) == T.TOPK_ERR_INVALID_ARG           # values
+    assert call(a1=None) == T.TOPK_ERR_INVALID_ARG           # ids
+    assert call(a9=None) == T.TOPK_ERR_INVALID_ARG           # out_ids
+    assert call(a2=0) == T.TOPK_ERR_INVALID_ARG              # C < 1
+    assert call(a3=0) == T.TOPK_ERR_INVALID_ARG              # k < 1
+    assert call(a3=65) == T.TOPK_ERR_INVALID_ARG             # k > TOPK_MAX_K
+    assert call(a4=2) == T.TOPK_ERR_INVALID_ARG              # dtype
+    assert call(a5=0.0) == T.TOPK_ERR_INVALID_ARG            # temperature
+    assert call(a5=float("inf")) == T.TOPK_ERR_INVALID_ARG
+    assert call(a6=0.0) == T.TOPK_ERR_INVALID_ARG            # top_p
+    assert call(a6=1.5) == T.TOPK_ERR_INVALID_ARG
+    assert call(a0=17) == T.TOPK_ERR_INVALID_ARG             # misaligned fp32 values
+    assert call(a10=18) == T.TOPK_ERR_INVALID_ARG            # misaligned out_pos
     assert lib.topk_cols_query(None, None, None, None, None) == T.TOPK_ERR_INVALID_ARG
 
 
