@@ -339,7 +339,7 @@ int topk_cols_sample(const void* values, const int32_t* ids, int64_t C, int32_t 
     if (((uintptr_t)values % es) != 0 || ((uintptr_t)ids % 4) != 0 || ((uintptr_t)out_ids % 4) != 0 ||
         ((uintptr_t)out_pos % 4) != 0)
         return TOPK_ERR_INVALID_ARG;
-    if ((C + 255) / 256 > 0x7FFFFFFF) return TOPK_ERR_UNSUPPORTED;
+    if ((C + 3) / 4 > 0x7FFFFFFF) return TOPK_ERR_UNSUPPORTED;  // one column per wave, four per workgroup
     topk::SampleArgs a;
     a.values = values;
     a.ids = ids;

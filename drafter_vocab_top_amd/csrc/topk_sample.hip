@@ -23,9 +23,11 @@
 // 3", SC 2011): counter (offset low, offset high, column, 0), key (seed low,
 // seed high), ten rounds; u = ((out0 << 32 | out1) >> 11) * 2^-53.
 //
-// One thread per column: k <= 64 sequential steps per thread, far from any
-// bound; the step exists to follow the top-k on the same stream without a
-// host round trip.
+// One wave per column.  Lane j computes w_j (one exp per lane, in
+// parallel); the sums must keep the sequential order, so every lane then
+// walks j = 0 .. k-1 with w_j broadcast from lane j and adds it when j <= its
+// own index: lane m ends with S_{m+1}, summed in exactly the order above.
+// Ballots find n and j*.
 #include "topk_device.hpp"
 #include "topk_internal.hpp"
 
@@ -34,6 +36,7 @@ namespace topk {
 namespace {
 
 constexpr int kSampleThreads = 256;
+constexpr int kSampleWaves = kSampleThreads / 64;  // one column per wave
 
 __device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
 #pragma unroll
@@ -85,56 +88,58 @@ __device__ __forceinline__ double stored_value(const typename DT::storage* v, in
     return (double)__builtin_bit_cast(float, b);
 }
 
+__device__ __forceinline__ double lane_value(double x, int lane) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ uint32_t first_lane(unsigned long long mask) {
+    return (uint32_t)__builtin_ctzll(mask);
+}
+
 template <class DT>
 __global__ __launch_bounds__(kSampleThreads) void topk_sample_kernel(SampleArgs a) {
 #pragma clang fp contract(off)
     using storage = typename DT::storage;
-    const int64_t c = (int64_t)blockIdx.x * kSampleThreads + threadIdx.x;
-    if (c >= a.C) return;
+    const uint32_t lane = threadIdx.x & 63u;
+    const int64_t c = (int64_t)blockIdx.x * kSampleWaves + (threadIdx.x >> 6);
+    if (c >= a.C) return;  // wave-uniform
     const int32_t k = a.k;
     const storage* v = static_cast<const storage*>(a.values) + c * k;
-    int32_t pick = 0;
+    uint32_t pick = 0;
     const double v0 = stored_value<DT>(v, 0);
     if (__builtin_isfinite(v0)) {
-        // w_j is recomputed in each sweep (the same operations give the same
-        // value), which keeps the k weights out of an indexed array
-        auto weight = [&](int32_t j) { return fixed_exp((stored_value<DT>(v, j) - v0) / a.temperature); };
-        double total = 0.0;
-        for (int32_t j = 0; j < k; ++j) total += weight(j);
-        const double need = a.top_p * total;
-        int32_t n = k;
-        double sn = total;  // S_k; the sweep below stops at the first S_m >= need (m <= k since top_p <= 1)
-        double s = 0.0;
-        for (int32_t m = 1; m <= k; ++m) {
-            s += weight(m - 1);
-            if (s >= need) {
-                n = m;
-                sn = s;
-                break;
-            }
+        const bool in = (int32_t)lane < k;
+        const double w = in ? fixed_exp((stored_value<DT>(v, lane) - v0) / a.temperature) : 0.0;
+        double acc = 0.0;  // S_{lane+1} (S_k for lanes >= k)
+        for (int32_t j = 0; j < k; ++j) {
+            const double wj = lane_value(w, j);
+            if (j <= (int32_t)lane) acc = acc + wj;
         }
+        const double total = lane_value(acc, k - 1);
+        const double need = a.top_p * total;
+        const unsigned long long reach = __ballot(in && acc >= need);
+        const uint32_t n = reach ? first_lane(reach) + 1u : (uint32_t)k;  // lane k-1 always reaches
+        const double sn = lane_value(acc, (int)n - 1);
         uint32_t ctr[4] = {(uint32_t)a.offset, (uint32_t)(a.offset >> 32), (uint32_t)c, 0u};
         philox4x32_10(ctr, (uint32_t)a.seed, (uint32_t)(a.seed >> 32));
         const double u = (double)((((uint64_t)ctr[0] << 32) | ctr[1]) >> 11) * 0x1.0p-53;
         const double target = u * sn;
-        double acc = 0.0;
-        pick = n - 1;
-        for (int32_t j = 0; j < n; ++j) {
-            acc += weight(j);
-            if (acc > target) {
-                pick = j;
-                break;
-            }
-        }
+        const unsigned long long above = __ballot(lane < n && acc > target);
+        pick = above ? first_lane(above) : n - 1u;  // u < 1 makes lane n-1 pass
     }
-    a.out_ids[c] = a.ids[c * k + pick];
-    if (a.out_pos) a.out_pos[c] = pick;
+    if (lane == 0) {
+        a.out_ids[c] = a.ids[c * k + pick];
+        if (a.out_pos) a.out_pos[c] = (int32_t)pick;
+    }
 }
 
 }  // namespace
 
 hipError_t launch_sample(int dtype, const SampleArgs& a, hipStream_t stream) {
-    const dim3 grid((uint32_t)((a.C + kSampleThreads - 1) / kSampleThreads)), block(kSampleThreads);
+    const dim3 grid((uint32_t)((a.C + kSampleWaves - 1) / kSampleWaves)), block(kSampleThreads);
     if (dtype == 0)
         hipLaunchKernelGGL(topk_sample_kernel<Bf16>, grid, block, 0, stream, a);
     else
