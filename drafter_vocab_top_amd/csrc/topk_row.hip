@@ -177,6 +177,11 @@ struct RowFilter<Bf16> {
     __device__ __forceinline__ static bool has_negative_nan(uint32_t acc, int half) {
         return ((acc >> (16 * half)) & 0xFFFFu) > 0xFF80u;
     }
+    // running signed maximum per half of already-masked words (x ^ m)
+    static constexpr uint32_t kSMin = 0x80008000u;
+    __device__ __forceinline__ static uint32_t smax(uint32_t acc, uint32_t y) {
+        return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(as_s16x2_r(acc), as_s16x2_r(y)));
+    }
 };
 
 template <>
@@ -202,6 +207,8 @@ struct RowFilter<F32> {
     __device__ __forceinline__ static bool passes(uint32_t t, int) { return t != 0u; }
     __device__ __forceinline__ static uint32_t umax(uint32_t acc, uint32_t x) { return max_u32(acc, x); }
     __device__ __forceinline__ static bool has_negative_nan(uint32_t acc, int) { return acc > 0xFF800000u; }
+    static constexpr uint32_t kSMin = 0x80000000u;
+    __device__ __forceinline__ static uint32_t smax(uint32_t acc, uint32_t y) { return (uint32_t)max_i32((int)acc, (int)y); }
 };
 
 __device__ __forceinline__ uint32_t word(const u32x4& v, int q) {
@@ -697,9 +704,54 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
             const u32x4 fmw = *reinterpret_cast<const u32x4*>(&sh.fm[g * CPV]);
             const u32x4 fqw = *reinterpret_cast<const u32x4*>(&sh.fq[g * CPV]);
             const uint32_t rbase = r_lo + p * per_pass + rsub;
+            // A pass whose rows all lie in the segment is first filtered per
+            // lane: the test is monotone, so the per-word maxima of the masked
+            // patterns over the pass's rows pass iff some row does.  Only the
+            // lanes that pass queue their row vectors, and the drain tests each
+            // element exactly.  When more lanes pass than the queue holds, the
+            // per-vector filter below runs instead.
+            bool filtered = false;
+            if (r_lo + (p + 1u) * per_pass <= r_hi) {  // the same for the whole workgroup
+                auto lane_maxima = [&](auto masked_tag) {
+                    constexpr bool MASKED = decltype(masked_tag)::value;
+                    uint32_t wm[4] = {F::kSMin, F::kSMin, F::kSMin, F::kSMin};
+#pragma unroll
+                    for (int i = 0; i < NV; ++i) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const uint32_t w = word(cur[i], q);
+                            wm[q] = F::smax(wm[q], MASKED ? w ^ word(fmw, q) : w);
+                            nanacc[q] = F::umax(nanacc[q], w);
+                        }
+                    }
+                    uint32_t any = 0;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) any |= F::test(wm[q], 0u, word(fqw, q));
+                    return any;
+                };
+                // thresholds above the zero class need no mask (m = 0)
+                const bool masked = __ballot((fmw.x | fmw.y | fmw.z | fmw.w) != 0u) != 0ull;
+                const uint32_t any = masked ? lane_maxima(std::integral_constant<bool, true>{})
+                                            : lane_maxima(std::integral_constant<bool, false>{});
+                const bool has = any != 0u && ncols != 0u;
+                const unsigned long long bal = __ballot(has);
+                const uint32_t nq = (uint32_t)__popcll(bal) * (uint32_t)NV;
+                if (nq <= (uint32_t)kRowQueue) {
+                    if (has) {
+                        const uint32_t base = lanes_below(bal) * (uint32_t)NV;
+#pragma unroll
+                        for (int i = 0; i < NV; ++i) {
+                            sh.qdata[wave][base + (uint32_t)i] = cur[i];
+                            sh.qmeta[wave][base + (uint32_t)i] = ((rbase + (uint32_t)i * kRowsPerStep) << 3) | g;
+                        }
+                    }
+                    flush(nq);
+                    filtered = true;
+                }
+            }
             uint32_t qcnt = 0;
 #pragma unroll
-            for (int i = 0; i < NV; ++i) {
+            for (int i = 0; i < NV && !filtered; ++i) {
                 const uint32_t r = rbase + (uint32_t)i * kRowsPerStep;
                 uint32_t any = 0;
 #pragma unroll
@@ -722,7 +774,7 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
                     }
                 }
             }
-            flush(qcnt);
+            if (!filtered) flush(qcnt);
         }
         __syncthreads();
 
@@ -883,7 +935,6 @@ hipError_t launch_scan(int nv, const RowArgs& a, hipStream_t stream) {
     const dim3 grid((uint32_t)((int64_t)a.tiles * a.S)), block(kBlock);
     switch (nv) {
         case 8: hipLaunchKernelGGL((topk_row_scan<DT, 8, CAP, KT>), grid, block, 0, stream, a); break;
-        case 16: hipLaunchKernelGGL((topk_row_scan<DT, 16, CAP, KT>), grid, block, 0, stream, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -904,10 +955,16 @@ hipError_t launch_row_dt(int nv, const RowArgs& a, hipStream_t stream) {
                               : launch_scan<DT, kRowCapLarge, RowKey64>(nv, a, stream);
     }
     if (e != hipSuccess) return e;
-    // keys per lane: S*k entries over 64 lanes
+    // keys per lane: S*k entries over 64 lanes, in the smallest register
+    // bucket that holds them (every slot is visited in the selection)
     const dim3 mgrid((uint32_t)((a.C + kWaves - 1) / kWaves));
-    if ((int64_t)a.S * a.k <= 1024)
+    const int64_t m = (int64_t)a.S * a.k;
+    if (m <= 16 * 64)
         hipLaunchKernelGGL((topk_row_merge<DT, 16>), mgrid, dim3(kBlock), 0, stream, a);
+    else if (m <= 20 * 64)
+        hipLaunchKernelGGL((topk_row_merge<DT, 20>), mgrid, dim3(kBlock), 0, stream, a);
+    else if (m <= 24 * 64)
+        hipLaunchKernelGGL((topk_row_merge<DT, 24>), mgrid, dim3(kBlock), 0, stream, a);
     else
         hipLaunchKernelGGL((topk_row_merge<DT, kRowMaxMergeKeys / 64>), mgrid, dim3(kBlock), 0, stream, a);
     return hipGetLastError();
