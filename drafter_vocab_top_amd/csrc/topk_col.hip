@@ -38,13 +38,14 @@
 // workgroup's (massive ties), send that pass to an exact path.  There, each
 // wave finds its own top-k by a wave-wide bit search over the keys.
 //
-// Cross-workgroup merge without cache-flushing fences.  Each workgroup
-// publishes its sorted k keys with device-scope atomic stores, which write
-// through the XCD's L2.  It then takes the column's ticket, a device-scope
-// atomic on a 128-byte line of its own.  Every key carries the run's tag, so
-// the workgroup that draws the last ticket reads the S lists with
-// device-scope loads.  It re-reads any slot whose tag is stale until that
-// store lands.  All four of its waves then select from the S*k keys: per-wave
+// Cross-workgroup merge without cache-flushing fences.  Each workgroup takes
+// the column's ticket, a device-scope atomic on a 128-byte line of its own,
+// and while the reply is in flight ranks its candidates and publishes its
+// sorted k keys with device-scope atomic stores, which write through the
+// XCD's L2.  Every key carries the run's tag, so the workgroup that draws
+// the last ticket reads the S lists with device-scope loads and re-reads any
+// slot whose tag is stale (a list that another workgroup, or this one, has
+// not yet published, or whose store has not landed) until it has.  All four of its waves then select from the S*k keys: per-wave
 // thresholds, one barrier, one rank count.  It writes the output and resets
 // the ticket for the next run.
 #include "topk_col_common.hpp"
@@ -437,14 +438,20 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
         }
     }
 
-    // ---- wave 0: rank the segment's candidates, publish the sorted list and
-    //      take the column's ticket (the stores precede the ticket in the
-    //      wave's program order) ----
+    // ---- wave 0: take the column's ticket, rank the segment's candidates
+    //      and publish the sorted list; the list's slots carry the run tag,
+    //      so the last ticket holder waits for any list not yet published ----
     const uint64_t sentinel = tag;  // order 0: below every real key
     uint64_t* parts = a.partials + (int64_t)c * S * k;
     if (wave == 0) {
         const uint32_t lane = tid;
         uint64_t* dst = parts + s * k;
+        // the ticket is taken first and its reply awaited only after the
+        // list is ranked and published: the round trip hides the rank
+        uint32_t old = 0;
+        if (lane == 0)
+            old = __hip_atomic_fetch_add(&a.tickets[c * kTicketStride], 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
         if (n_last <= 64u) {
             const uint64_t key = lane < n_last ? sh.cand[lane] : 0ull;
             const uint32_t r = wave_rank_of(key, n_last);
@@ -456,11 +463,7 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
         }
         if (lane >= min_u32(n_last, k) && lane < k)
             __hip_atomic_store(&dst[lane], sentinel, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (lane == 0) {
-            const uint32_t old = __hip_atomic_fetch_add(&a.tickets[c * kTicketStride], 1u,
-                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            sh.is_last = old == S - 1u ? 1u : 0u;
-        }
+        if (lane == 0) sh.is_last = old == S - 1u ? 1u : 0u;
     }
     __syncthreads();
     if (!sh.is_last) return;
