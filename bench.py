@@ -329,7 +329,7 @@ def _counter_rows(directory, counter):
     return rows
 
 
-def summarize_counters(fetch_dir, write_dir, config_n):
+def summarize_counters(fetch_dir, write_dir, config_n, out_path=None):
     """HBM bytes per launch of the top-k kernels from FETCH_SIZE and WRITE_SIZE
     (KiB per dispatch), each scaled by what the same counter reads for the
     calibration copy of COPY_BYTES that ends a '--profile' run (the last five
@@ -361,12 +361,13 @@ def summarize_counters(fetch_dir, write_dir, config_n):
     out["hbm_bytes_per_launch"] = round(per_launch)
     out["algorithmic_bytes"] = algorithmic_bytes(w)
     out["ratio_to_algorithmic"] = per_launch / out["algorithmic_bytes"]
-    path = traffic_path(w, config_n)
+    path = out_path or traffic_path(w, config_n)
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out, indent=1))
     log(f"wrote {path}")
+    return out
 
 
 def traffic_record(digest, w, config_n):

@@ -257,7 +257,6 @@ template <class DT, int NV>
 __global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
     using storage = typename DT::storage;
     constexpr int EPV = DT::kPerVec;
-    constexpr int OB = DT::kOrderBits;
     __shared__ ColShared sh;
 
     const uint32_t tid = threadIdx.x, wave = tid >> 6;

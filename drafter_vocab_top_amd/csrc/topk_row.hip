@@ -494,7 +494,6 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
     constexpr int TW = RowTile<DT>::TW;
     constexpr int CPV = RowTile<DT>::CPV;
     constexpr int TPC = RowTile<DT>::TPC;
-    constexpr int OB = DT::kOrderBits;
     static_assert(NV % 2 == 0, "two row groups per pass");
     __shared__ RowShared<DT, CAP, KT> sh;
 
