@@ -594,12 +594,29 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
     // how many loads are in flight, so filtering a pass waits for that pass
     // alone while the next one streams in.
     const bool full_tile = a.vec_loads != 0 && c0 + (uint32_t)TW <= C;
+    // Byte offsets from the segment's first row fit 32 bits (and a 24 x 24-bit
+    // multiply) in every realistic shape; the row address is then one 24-bit
+    // multiply-add on a uniform base instead of 64-bit arithmetic per load.
+    const uint64_t row_bytes = (uint64_t)a.ld * sizeof(storage);
+    const bool off24 = row_bytes < (1u << 24) && (uint64_t)(r_hi - r_lo) * row_bytes + 128u < (1ull << 31);
+    const char* seg_bytes = reinterpret_cast<const char*>(x + (int64_t)r_lo * a.ld + c0);
+    const uint32_t lane_bytes = (cg - c0) * (uint32_t)sizeof(storage);
     auto load_full = [&](u32x4(&d)[NV], uint32_t p, uint32_t step) {
         const uint32_t rbase = r_lo + p * per_pass + rsub;
+        if (off24) {
+            const uint32_t rb = (uint32_t)row_bytes, rel = rbase - r_lo, last = r_hi - 1u - r_lo;
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const uint32_t r = min_u32(rbase + (uint32_t)i * step, r_hi - 1u);
-            d[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + (int64_t)r * a.ld + cg));
+            for (int i = 0; i < NV; ++i) {
+                const uint32_t rr = min_u32(rel + (uint32_t)i * step, last);
+                const uint32_t off = __umul24(rr, rb) + lane_bytes;
+                d[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(seg_bytes + off));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const uint32_t r = min_u32(rbase + (uint32_t)i * step, r_hi - 1u);
+                d[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + (int64_t)r * a.ld + cg));
+            }
         }
     };
     const u32x4 fill4 = u32x4{DT::kFillDword, DT::kFillDword, DT::kFillDword, DT::kFillDword};
