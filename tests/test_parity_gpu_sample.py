@@ -95,3 +95,44 @@ def test_sample_refuses_bad_arguments(gpu):
                                 None, None) == T.TOPK_ERR_INVALID_ARG
     assert lib.topk_cols_sample(None, ids.data_ptr(), 4, 8, 1, 1.0, 0.9, 0, 0, out.data_ptr(),
                                 None, None) == T.TOPK_ERR_INVALID_ARG
+
+
+def test_graph_replay_of_topk_and_sample(gpu):
+    """A row-interleaved top-k followed by the sampler, captured in one graph
+    and replayed with alternating inputs (eager copies and host syncs between
+    replays): every replay's draws equal the oracle's.  The sampler keeps no
+    state, and the row layout's run clears what it shares."""
+    torch, T = gpu
+    V, C, k = 40009, 70, 16
+    temp, p, seed, offset = 1.0, 0.95, 77, 5
+    xs = [W.random_matrix(500 + i, V, C, W.BF16, W.ROW, kind="normal") for i in range(2)]
+    expect = []
+    for x in xs:
+        ov, oi = run_oracle(x, V, C, k, W.BF16, W.ROW, C)
+        expect.append(oracle.sample_topk(ov, oi, C, k, oracle.BF16, temp, p, seed, offset))
+    src = to_device(torch, xs[0])
+    staged = [to_device(torch, x) for x in xs]
+    with T.TopkCols(V, C, k, W.BF16, W.ROW, C) as h:
+        vals = torch.empty((C, k), dtype=torch.int16, device="cuda")
+        ids = torch.empty((C, k), dtype=torch.int32, device="cuda")
+        sid = torch.empty(C, dtype=torch.int32, device="cuda")
+        pos = torch.empty(C, dtype=torch.int32, device="cuda")
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            h.run(src, vals, ids)
+            T.sample(vals, ids, temp, p, seed, offset, sid, pos)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            h.run(src, vals, ids, stream=stream)
+            T.sample(vals, ids, temp, p, seed, offset, sid, pos, stream=stream)
+        for rep in range(6):
+            i = rep % 2
+            src.copy_(staged[i])
+            torch.cuda.synchronize()
+            print(f"[parity] graph replay {rep} input {i}", flush=True)
+            g.replay()
+            torch.cuda.synchronize()
+            eid, epos = expect[i]
+            assert np.array_equal(pos.cpu().numpy(), epos), rep
+            assert np.array_equal(sid.cpu().numpy(), eid), rep
