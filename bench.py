@@ -394,7 +394,7 @@ def main():
     ap.add_argument("--profile", type=int, nargs="?", const=HEADLINE, default=None, metavar="N",
                     help="profiling run: workload N only (default: the headline), few steps, "
                          "plus a plain copy of known size")
-    ap.add_argument("--algo", default="auto", choices=["auto", "workgroup", "wave", "one_wave"],
+    ap.add_argument("--algo", default="auto", choices=["auto", "workgroup", "one_wave"],
                     help="kernel family for a --profile run (column-contiguous workloads)")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "N"),
                     help="turn the counter_collection.csv files of a FETCH_SIZE and a WRITE_SIZE "

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libtopk_cols.so")
-SOURCES = [os.path.join(CSRC, n) for n in ("topk_col.hip", "topk_colw.hip", "topk_row.hip", "topk_onewave.hip",
+SOURCES = [os.path.join(CSRC, n) for n in ("topk_col.hip", "topk_row.hip", "topk_onewave.hip",
                                             "topk_sample.hip", "topk_cols_api.cpp")]
 OBJDIR = os.path.join(ROOT, "_build")
 # Per-source flags.  The column kernel takes its ticket before ranking and

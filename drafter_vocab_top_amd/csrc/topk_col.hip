@@ -42,12 +42,24 @@
 // the column's ticket, a device-scope atomic on a 128-byte line of its own,
 // and while the reply is in flight ranks its candidates and publishes its
 // sorted k keys with device-scope atomic stores, which write through the
-// XCD's L2.  Every key carries the run's tag, so the workgroup that draws
-// the last ticket reads the S lists with device-scope loads and re-reads any
-// slot whose tag is stale (a list that another workgroup, or this one, has
-// not yet published, or whose store has not landed) until it has.  All four of its waves then select from the S*k keys: per-wave
-// thresholds, one barrier, one rank count.  It writes the output and resets
-// the ticket for the next run.
+// XCD's L2.  Every key carries the run's tag in its low byte, so the
+// workgroup that draws the last ticket reads the S lists with device-scope
+// loads and re-reads any slot whose tag is not the run's (a list that
+// another workgroup, or this one, has not yet published, or whose store has
+// not landed) until it is.  All four of its waves then select from the S*k
+// keys: per-wave thresholds, one barrier, one rank count.  It writes the
+// output and sets the ticket back to zero.
+//
+// The run's tag lives in device memory, next to the column's ticket: every
+// workgroup reads it as it starts (the read travels with the data), and the
+// merger advances it (1, 2, ..., 255, 1, ...) when it resets the ticket.  A
+// list slot not yet rewritten in a run still holds the previous run's tag,
+// so the state a run starts from needs no reset, and a captured launch
+// replays correctly.  When the workspace is shared by runs of different
+// shapes (the entry point that allocates nothing), the tag stays 1 and the
+// merger sets the column's list slots back to zero instead.  The merger's
+// wait is bounded; if it gives up, it raises the workspace's error word,
+// which the host reports, and writes no output.
 #include "topk_col_common.hpp"
 #include "topk_device.hpp"
 #include "topk_internal.hpp"
@@ -61,7 +73,6 @@ static_assert(kWaves == kColWavesPerBlock, "host and kernel disagree on waves pe
 constexpr int kWaveCap = 192;                // candidate slots per wave
 constexpr int kBlockCap = 512;               // carried best + candidates per workgroup
 constexpr int kMergeKeysPerThread = 16;      // S*k <= 4096 published keys, 16 per thread
-constexpr int kSpinLimit = 1 << 16;          // about 0.1 s: a store that has not landed by then never will
 constexpr int kQueue = 128;                  // queued vectors per wave
 constexpr int kWaveMergeKeys = 1024;         // wave 0 alone merges up to this many published keys
 
@@ -118,13 +129,25 @@ __device__ __noinline__ uint32_t exact_scan_wave(uint64_t* wb, uint64_t* out, co
     return wave_exact_topk<DT::kOrderBits>(wb, kWaveCap, out, visit, k);
 }
 
+// Re-reads a published slot until its key carries the run's tag (only the
+// lanes still waiting take part, one read in flight each).  Returns true
+// when the bounded wait gave up.
+__device__ __forceinline__ bool wait_tag(const ColArgs& a, const uint64_t* p, uint32_t tag, uint64_t& key) {
+    for (uint32_t spin = 0; key_tag(key) != tag || a.fail_waits != 0; ++spin) {
+        if (spin >= a.spin_limit) return true;
+        __builtin_amdgcn_s_sleep(1);
+        key = load_published(p);
+    }
+    return false;
+}
+
 // Selection by the last workgroup of a column: the top k of the S*k
 // published keys, into sh.best.
 template <class DT>
-__device__ __forceinline__ void merge_lists(const ColArgs& a, ColShared& sh, const uint64_t* parts) {
+__device__ __forceinline__ bool merge_lists(const ColArgs& a, ColShared& sh, const uint64_t* parts, uint32_t tag) {
     constexpr int OB = DT::kOrderBits;
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
-    const uint32_t k = (uint32_t)a.k, tag = a.tag;
+    const uint32_t k = (uint32_t)a.k;
     const uint32_t M = (uint32_t)a.S * k;
     // slots j < J hold keys (J = M / 256 rounded up; the later slots are skipped
     // by a workgroup-uniform test)
@@ -136,15 +159,15 @@ __device__ __forceinline__ void merge_lists(const ColArgs& a, ColShared& sh, con
         keys[j] = 0;
         if ((uint32_t)j < J && idx < M) keys[j] = load_published(parts + idx);
     }
+    bool gave_up = false;
 #pragma unroll
     for (int j = 0; j < kMergeKeysPerThread; ++j) {
         const uint32_t idx = tid + (uint32_t)j * kBlock;
-        if ((uint32_t)j < J && idx < M) {
-            for (int spin = 0; key_tag(keys[j]) != tag && spin < kSpinLimit; ++spin) {
-                __builtin_amdgcn_s_sleep(1);
-                keys[j] = load_published(parts + idx);
-            }
-        }
+        if ((uint32_t)j < J && idx < M) gave_up |= wait_tag(a, parts + idx, tag, keys[j]);
+    }
+    if (__syncthreads_or(gave_up)) {
+        if (tid == 0) __hip_atomic_fetch_or(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return false;
     }
     uint64_t rep = 0;
 #pragma unroll
@@ -194,6 +217,7 @@ __device__ __forceinline__ void merge_lists(const ColArgs& a, ColShared& sh, con
     }
     rank_select(sh.cand, n, k, sh.best, tid, kBlock);
     __syncthreads();
+    return true;
 }
 
 // Selection by wave 0 of the column's last workgroup when the S*k published
@@ -202,12 +226,12 @@ __device__ __forceinline__ void merge_lists(const ColArgs& a, ColShared& sh, con
 // scalar broadcasts when at most 64), and out(position, key) writes each of
 // the top k.
 template <class DT, class Out>
-__device__ __forceinline__ void merge_lists_wave(const ColArgs& a, ColShared& sh, const uint64_t* parts,
-                                                 const Out& out) {
+__device__ __forceinline__ bool merge_lists_wave(const ColArgs& a, ColShared& sh, const uint64_t* parts,
+                                                 uint32_t tag, const Out& out) {
     constexpr int OB = DT::kOrderBits;
     constexpr int RMAX = kWaveMergeKeys / 64;
     const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t k = (uint32_t)a.k, tag = a.tag;
+    const uint32_t k = (uint32_t)a.k;
     const uint32_t M = (uint32_t)a.S * k;
     const uint32_t R = (M + 63u) / 64u;  // wave-uniform
     uint64_t keys[RMAX];
@@ -217,15 +241,15 @@ __device__ __forceinline__ void merge_lists_wave(const ColArgs& a, ColShared& sh
         keys[j] = 0;
         if ((uint32_t)j < R && idx < M) keys[j] = load_published(parts + idx);
     }
+    bool gave_up = false;
 #pragma unroll
     for (int j = 0; j < RMAX; ++j) {
         const uint32_t idx = (uint32_t)j * 64u + lane;
-        if ((uint32_t)j < R && idx < M) {
-            for (int spin = 0; key_tag(keys[j]) != tag && spin < kSpinLimit; ++spin) {
-                __builtin_amdgcn_s_sleep(1);
-                keys[j] = load_published(parts + idx);
-            }
-        }
+        if ((uint32_t)j < R && idx < M) gave_up |= wait_tag(a, parts + idx, tag, keys[j]);
+    }
+    if (__any(gave_up)) {
+        if (lane == 0) __hip_atomic_fetch_or(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return false;
     }
     uint64_t rep = 0;
 #pragma unroll
@@ -246,11 +270,12 @@ __device__ __forceinline__ void merge_lists_wave(const ColArgs& a, ColShared& sh
         const uint64_t key = lane < cnt ? sh.cand[lane] : 0ull;
         const uint32_t r = wave_rank_of(key, cnt);
         if (lane < cnt && r < k) out(r, key);
-        return;
+        return true;
     }
     const uint32_t n = cnt > (uint32_t)kBlockCap ? wave_exact_topk<OB>(sh.wbuf[0], kWaveCap, sh.best, visit, k)
                                                  : wave_rank_select(sh.cand, cnt, k, sh.best);
     if (lane < n) out(lane, sh.best[lane]);
+    return true;
 }
 
 template <class DT, int NV>
@@ -261,7 +286,6 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
 
     const uint32_t tid = threadIdx.x, wave = tid >> 6;
     const uint32_t k = (uint32_t)a.k;
-    const uint32_t tag = a.tag;
     // Rows and vector indices fit in 32 bits (V < 2^24); only the column
     // offset c * ld needs 64.
     const uint32_t S = (uint32_t)a.S;
@@ -269,6 +293,13 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
     const uint32_t s = blockIdx.x - c * S;
     const uint32_t V = (uint32_t)a.V;
     const storage* col = static_cast<const storage*>(a.x) + (int64_t)c * a.ld;
+    // The column's ticket and the run's tag share a 128-byte line: word 0
+    // counts the workgroups that finished, word 1 holds the run count
+    // modulo 255 (the tag is one more).  Read before any data load; the
+    // read travels with the data.
+    uint32_t* ticket = a.tickets + c * kTicketStride;
+    const uint32_t epoch_v = __hip_atomic_load(ticket + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t epoch = 0, tag = 0;  // taken from epoch_v once the first pass's data are in
 
     // Split the column into an unaligned head, 16-byte vectors and a tail.
     uint32_t head = ((16u - ((uint32_t)(uintptr_t)col & 15u)) & 15u) / (uint32_t)sizeof(storage);
@@ -283,7 +314,7 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
         uint32_t row = 0xFFFFFFFFu;
         if (s == 0 && tid < head) row = tid;
         if (s == S - 1 && tid >= 32 && tid - 32 < V - tail0) row = tail0 + (tid - 32);
-        if (row != 0xFFFFFFFFu) edge = make_key(DT::order(col[row]), row, tag);
+        if (row != 0xFFFFFFFFu) edge = make_key(DT::order(col[row]), row, 0u);  // tagged in pass 0
     }
     if (tid == 0) {
         sh.ncand = 0;
@@ -309,12 +340,15 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
         }
         // vector slots of this lane that hold data
         const int nvalid = ve > v0 ? (int)min_u32((uint32_t)NV, (ve - v0 + kBlock - 1) / kBlock) : 0;
-        const uint64_t ex = p == 0 ? edge : 0;
-
         uint32_t vmax[NV];
         uint32_t rep;
         bool neg_nan;
         lane_stats<DT, NV>(d, vmax, rep, neg_nan);
+        if (p == 0) {
+            epoch = (uint32_t)__builtin_amdgcn_readfirstlane((int)epoch_v);
+            tag = epoch + 1u;
+        }
+        const uint64_t ex = p == 0 && edge != 0 ? edge | tag : 0;
         if (ex) rep = max_u32(rep, key_order(ex));
         // Each wave's k-th largest lane maximum bounds the workgroup's k-th
         // largest element from below, so the largest of the four does too.
@@ -448,9 +482,7 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
         // the ticket is taken first and its reply awaited only after the
         // list is ranked and published: the round trip hides the rank
         uint32_t old = 0;
-        if (lane == 0)
-            old = __hip_atomic_fetch_add(&a.tickets[c * kTicketStride], 1u, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (n_last <= 64u) {
             const uint64_t key = lane < n_last ? sh.cand[lane] : 0ull;
             const uint32_t r = wave_rank_of(key, n_last);
@@ -475,15 +507,29 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
                                                                   : DT::bits_from_order(o));
         a.out_ids[(int64_t)c * k + pos] = a.id_map ? a.id_map[row] : (int32_t)row;
     };
+    bool ok;
+    uint32_t first, stride;
     if ((uint32_t)a.S * k <= (uint32_t)kWaveMergeKeys) {
         if (wave != 0) return;
-        merge_lists_wave<DT>(a, sh, parts, write_out);
+        ok = merge_lists_wave<DT>(a, sh, parts, tag, write_out);
+        first = tid;
+        stride = 64u;
     } else {
-        merge_lists<DT>(a, sh, parts);
-        if (tid < k) write_out(tid, sh.best[tid]);
+        ok = merge_lists<DT>(a, sh, parts, tag);
+        if (ok && tid < k) write_out(tid, sh.best[tid]);
+        first = tid;
+        stride = kBlock;
     }
-    if (tid == 0)
-        __hip_atomic_store(&a.tickets[c * kTicketStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Every list of the run has landed (the merger saw all of them).  The
+    // next run of the column starts from a zero ticket and the next tag; in
+    // a workspace shared between shapes the lists go back to zero instead.
+    // (After a wait that gave up, the host resets the workspace.)
+    if (a.clear_lists && ok)
+        for (uint32_t idx = first; idx < S * k; idx += stride) __hip_atomic_store(parts + idx, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+        const uint64_t next = a.clear_lists ? (uint64_t)epoch : (uint64_t)(epoch + 1u == 255u ? 0u : epoch + 1u);
+        __hip_atomic_store(reinterpret_cast<uint64_t*>(ticket), next << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 template <class DT>

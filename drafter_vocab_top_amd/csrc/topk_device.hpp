@@ -10,9 +10,11 @@
 // order.  A candidate is a 64-bit key:
 //     [63:32] order of the value
 //     [31: 8] 0xFFFFFF - row     (so the smaller row is the larger key)
-//     [ 7: 0] run tag            (equal for every key of one run)
+//     [ 7: 0] run tag            (equal for every key of one run; the
+//                                 column kernel's cross-workgroup lists)
 // Rows are distinct within a column, so keys of one column are distinct and
-// the key order is strict and total: the top-k is unique.
+// the key order is strict and total: the top-k is unique.  No element has
+// order 0.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -142,6 +144,18 @@ __device__ __forceinline__ uint32_t wave_kth_largest(uint32_t v, uint32_t k) {
     return t;
 }
 
+// Maximum of one unsigned value per lane over a full wave, through DPP lane
+// moves (row shifts within rows of 16, then row broadcasts): wave-uniform.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max_u32(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x111, 0xF, 0xF, false));  // row_shr:1
+    v = max_u32(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x112, 0xF, 0xF, false));  // row_shr:2
+    v = max_u32(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x114, 0xF, 0xF, false));  // row_shr:4
+    v = max_u32(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x118, 0xF, 0xF, false));  // row_shr:8
+    v = max_u32(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+    v = max_u32(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // Number of lanes below this one whose bit is set in `mask`.
 __device__ __forceinline__ uint32_t lanes_below(unsigned long long mask) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
@@ -164,13 +178,14 @@ __device__ __forceinline__ uint32_t wave_append(KeyT* buf, uint32_t cnt, uint32_
 typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
 // Rank selection: keys[0..n) are distinct keys in LDS (16-byte aligned,
-// readable up to n rounded up to 8).  The key of rank r (r < k, rank 0 =
-// largest) is written to out[r]; returns min(n, k).  A key's rank is the
-// number of keys above it.  Threads first, first + stride, ... take one key
-// each; all of them read the same eight keys per step with 16-byte LDS reads
-// (broadcasts), so the count is not bound by the latency of one read per key.
-__device__ __forceinline__ uint32_t rank_select(const uint64_t* keys, uint32_t n, uint32_t k,
-                                                uint64_t* out, uint32_t first, uint32_t stride) {
+// readable up to n rounded up to 8).  For the key of rank r (r < k, rank 0 =
+// largest) it calls f(r, key).  A key's rank is the number of keys above it.
+// Threads first, first + stride, ... take one key each; all of them read the
+// same eight keys per step with 16-byte LDS reads (broadcasts), so the count
+// is not bound by the latency of one read per key.
+template <class F>
+__device__ __forceinline__ void rank_apply(const uint64_t* keys, uint32_t n, uint32_t k, uint32_t first,
+                                           uint32_t stride, const F& f) {
     const uint32_t n8 = (n + 7u) & ~7u;
     for (uint32_t t = first; t < n; t += stride) {
         const uint64_t key = keys[t];
@@ -187,8 +202,14 @@ __device__ __forceinline__ uint32_t rank_select(const uint64_t* keys, uint32_t n
                  (v4 > key && j + 4 < n) + (v5 > key && j + 5 < n) +
                  (v6 > key && j + 6 < n) + (v7 > key && j + 7 < n);
         }
-        if (r < k) out[r] = key;
+        if (r < k) f(r, key);
     }
+}
+
+// rank_apply that writes the key of rank r to out[r]; returns min(n, k).
+__device__ __forceinline__ uint32_t rank_select(const uint64_t* keys, uint32_t n, uint32_t k,
+                                                uint64_t* out, uint32_t first, uint32_t stride) {
+    rank_apply(keys, n, k, first, stride, [&](uint32_t r, uint64_t key) { out[r] = key; });
     return min_u32(n, k);
 }
 
@@ -236,6 +257,8 @@ __device__ __forceinline__ uint32_t wave_exact_topk(uint64_t* buf, uint32_t cap,
     visit([&](uint64_t, bool valid) { total += (uint32_t)__popcll(__ballot(valid)); });
     uint64_t thr = 0;
     if (total > k) {
+        // a rare path: the rounds stay a loop, so the code stays small
+#pragma unroll 1
         for (int b = 32 + OrderBits - 1; b >= 8; --b) {
             const uint64_t cand = thr | (1ull << b);
             uint32_t n = 0;

@@ -18,9 +18,12 @@ struct ColArgs {
     int32_t C;
     int32_t k;
     int32_t S;            // vocabulary segments (workgroups) per column, <= kMaxSegments
-    uint32_t tag;         // 1..255, differs between consecutive runs of a handle
+    uint32_t spin_limit;  // re-reads of a list slot before the merger gives up
+    uint32_t fail_waits;  // tests only: the merger treats every list as not yet published
+    uint32_t clear_lists; // 1: the workspace is shared between shapes (keep tag 1, zero the lists after a run)
     uint64_t* partials;   // C*S*k keys: one list of k per workgroup
-    uint32_t* tickets;    // C counters kTicketStride apart, zero between runs
+    uint32_t* tickets;    // per column, kTicketStride apart: a counter (zero between runs) and the run count mod 255
+    uint32_t* error;      // set nonzero when a merger's wait gave up
     void* out_values;     // C*k elements of the input dtype
     int32_t* out_ids;     // C*k
     const int32_t* id_map;  // NULL, or V entries: out_ids holds id_map[row] instead of row
@@ -39,16 +42,9 @@ constexpr int kColVecChoices[3] = {2, 4, 8};
 // dtype: TOPK_BF16 or TOPK_F32; nv: one of kColVecChoices.
 hipError_t launch_col(int dtype, int nv, const ColArgs& a, hipStream_t stream);
 
-// Column-contiguous, one wave per vocabulary segment: the same arguments,
-// with S workgroups per column and 4*S wave segments, each publishing a list
-// (partials holds C*4*S*k keys).  The last wave of a column merges
-// 4*S*k <= kWaveSegMergeKeys keys.
-constexpr int kWaveSegMergeKeys = 2048;
-hipError_t launch_colw(int dtype, int nv, const ColArgs& a, hipStream_t stream);
-
 // Column-contiguous, one wave per column and no vocabulary split (the
-// baseline design): C workgroups of 64 lanes; S, tag, partials and tickets
-// are not used.
+// baseline design): C workgroups of 64 lanes; S, partials, tickets and the
+// wait fields are not used.
 hipError_t launch_onewave(int dtype, const ColArgs& a, hipStream_t stream);
 
 // Row-interleaved launch: element (r, c) at x[r*ld + c].  The scan grid is
@@ -96,5 +92,38 @@ hipError_t launch_sample(int dtype, const SampleArgs& a, hipStream_t stream);
 // Columns per tile for a dtype (128 bytes of a row).
 int row_tile_columns(int dtype);
 hipError_t launch_row(int dtype, int nv, const RowArgs& a, hipStream_t stream);
+
+// ------------------------------------------------------------ host side ---
+
+// The launch decomposition of one shape and the layout of its workspace, as
+// chosen for a device.  Built by make_plan; used by a handle and by the
+// entry point that runs in a caller-free static workspace.
+struct Plan {
+    int64_t V, C, ld;
+    int32_t k, dtype, layout;
+    int32_t algo;          // topk_algo of the column-contiguous layout (AUTO for the row layout)
+    int64_t segments;      // workgroups per column, or row segments
+    int64_t blocks;        // workgroups of the main kernel
+    int64_t tiles;         // column tiles (row layout)
+    int nv;                // 16-byte vectors (row steps) per lane per pass
+    // workspace: [error word][tickets][lists][bound], each part 256-byte aligned
+    size_t error_off, ticket_off, list_off, bound_off, workspace_bytes;
+};
+
+// Validates a shape (the rules of topk_cols_create) and fills plan for a
+// device with cu_count CUs.  Returns a topk_status.
+int make_plan(Plan* plan, int64_t V, int64_t C, int32_t k, int32_t dtype, int32_t layout, int64_t ld,
+              int64_t forced_segments, int32_t algo, int cu_count);
+
+// Enqueues one run over the first n_cols columns (0 < n_cols <= plan.C)
+// with the workspace at ws (plan.workspace_bytes, zero where the kernels
+// expect zeros).  Pointers are checked by the caller.  Returns a HIP error.
+hipError_t launch_plan(const Plan& plan, void* ws, int64_t n_cols, const void* logits, const int32_t* id_map,
+                       void* out_values, int32_t* out_ids, uint32_t spin_limit, uint32_t fail_waits,
+                       uint32_t clear_lists, hipStream_t stream);
+
+// Re-reads of a list slot before a merging workgroup gives up (each costs a
+// device round trip of about a microsecond: tens of milliseconds in all).
+constexpr uint32_t kDefaultSpinLimit = 1u << 16;
 
 }  // namespace topk

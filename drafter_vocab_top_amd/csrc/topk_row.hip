@@ -127,6 +127,7 @@ struct RowShared {
     uint32_t thr[TW];                            // running threshold per column (order)
     uint32_t cnt[TW];                            // candidates per column (may exceed CAP)
     uint32_t flag[TW];                           // 1: candidates overflowed, 2: negative NaN seen
+    uint32_t ovf;                                // some column overflowed in this pass
 };
 
 __device__ __forceinline__ s16x2 as_s16x2_r(uint32_t w) { return __builtin_bit_cast(s16x2, w); }
@@ -524,6 +525,7 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
         sh.cnt[tid] = 0;
         sh.flag[tid] = 0;
     }
+    if (tid == 0) sh.ovf = 0;
 
     const uint32_t per_pass = (uint32_t)kRowsPerStep * NV;
     const uint32_t npass = r_hi > r_lo ? (r_hi - r_lo + per_pass - 1) / per_pass : 0u;
@@ -582,6 +584,7 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
                     const uint32_t o = DT::order(row_elem<DT>(d, j));
                     const uint32_t pos = atomicAdd(&sh.cnt[col], 1u);
                     if (pos < (uint32_t)CAP) sh.cand[col][pos] = KT::make(o, row, r_lo);
+                    else sh.ovf = 1u;
                 }
             }
         }
@@ -819,10 +822,12 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
             for (int j = 0; j < kBoundPerThread; ++j)
                 if (pq * kBoundPerThread + (uint32_t)j < k) bmin = min_u32(bmin, slot[j]);
             const uint32_t Tg = group_min<TPC>(bmin);
-            if (a.use_bound && p + 1 < npass && Tg > sh.thr[pcol]) {
+            // (an overflowed column is left to the rebuild below; the bound
+            // applies to it from the next pass on)
+            if (a.use_bound && p + 1 < npass && Tg > sh.thr[pcol] && sh.cnt[pcol] <= (uint32_t)CAP) {
                 // candidates below the raised threshold can go at once
                 const uint32_t nc = sh.cnt[pcol];
-                const uint32_t kept = nc <= (uint32_t)CAP ? cull_column<DT, KT>(sh.cand[pcol], pq, nc, Tg) : nc;
+                const uint32_t kept = cull_column<DT, KT>(sh.cand[pcol], pq, nc, Tg);
                 if (pq == 0) {
                     uint32_t fmv, fqv;
                     F::encode(Tg, fmv, fqv);
@@ -832,15 +837,23 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
                     sh.cnt[pcol] = kept;
                 }
             }
-            const uint32_t pass_lo = r_lo + p * per_pass;
-            const uint32_t pass_hi = min_u32(pass_lo + per_pass, r_hi);
-            uint64_t todo = wave_columns<TW>(wave, [&](uint32_t colx) {
-                return c0 + colx < C && sh.cnt[colx] > (uint32_t)CAP && (sh.flag[colx] & 1u) == 0u;
-            });
-            while (todo) {
-                const uint32_t colx = wave + (uint32_t)__builtin_ctzll(todo) * kWaves;
-                todo &= todo - 1ull;
-                rebuild_column<DT, NV, CAP, KT>(sh, x, a.ld, colx, c0 + colx, r_lo, pass_lo, pass_hi, k);
+            // sh.ovf was set before the barrier that ended (2), so every
+            // thread reads the same value.  The rebuild of a column runs in
+            // another wave than the threads that own its trim and bound step
+            // above: a barrier separates the two.
+            if (sh.ovf) {
+                __syncthreads();
+                if (tid == 0) sh.ovf = 0u;
+                const uint32_t pass_lo = r_lo + p * per_pass;
+                const uint32_t pass_hi = min_u32(pass_lo + per_pass, r_hi);
+                uint64_t todo = wave_columns<TW>(wave, [&](uint32_t colx) {
+                    return c0 + colx < C && sh.cnt[colx] > (uint32_t)CAP && (sh.flag[colx] & 1u) == 0u;
+                });
+                while (todo) {
+                    const uint32_t colx = wave + (uint32_t)__builtin_ctzll(todo) * kWaves;
+                    todo &= todo - 1ull;
+                    rebuild_column<DT, NV, CAP, KT>(sh, x, a.ld, colx, c0 + colx, r_lo, pass_lo, pass_hi, k);
+                }
             }
         }
         if (p + 1 < npass) {

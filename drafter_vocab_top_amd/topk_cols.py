@@ -24,6 +24,7 @@ TOPK_ERR_INVALID_ARG = -1
 TOPK_ERR_UNSUPPORTED = -2
 TOPK_ERR_HIP = -3
 TOPK_ERR_OUT_OF_MEMORY = -4
+TOPK_ERR_TIMEOUT = -5
 TOPK_MAX_K = 64
 TOPK_MAX_V = (1 << 24) - 1
 
@@ -32,10 +33,11 @@ LAYOUTS = {"col": 0, "row": 1}
 
 EXPORTED = ("topk_cols_create", "topk_cols_create_with_segments", "topk_cols_create_tuned",
             "topk_cols_run", "topk_cols_run_n", "topk_cols_run_mapped", "topk_cols_sample",
-            "topk_cols_destroy", "topk_cols_status_string", "topk_cols_query")
+            "topk_cols_destroy", "topk_cols_status_string", "topk_cols_query", "topk_cols_check",
+            "topk_cols_debug_fail_waits")
 # kernel families of the column-contiguous layout ("one_wave": the baseline
 # design with one wave per column and no vocabulary split)
-ALGOS = {"auto": 0, "workgroup": 1, "wave": 2, "one_wave": 3}
+ALGOS = {"auto": 0, "workgroup": 1, "one_wave": 3}
 
 _lib = None
 
@@ -77,6 +79,10 @@ def load(path: str = LIBRARY):
     lib.topk_cols_query.argtypes = [p, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64),
                                     ctypes.POINTER(i32)]
     lib.topk_cols_query.restype = ctypes.c_int
+    lib.topk_cols_check.argtypes = [p]
+    lib.topk_cols_check.restype = ctypes.c_int
+    lib.topk_cols_debug_fail_waits.argtypes = [p, i32]
+    lib.topk_cols_debug_fail_waits.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -102,8 +108,11 @@ class TopkCols:
         self.ld = ld if ld is not None else (V if layout == "col" else C)
         lib = load()
         self._h = ctypes.c_void_p()
-        rc = lib.topk_cols_create_tuned(ctypes.byref(self._h), V, C, k, DTYPES[dtype],
-                                        LAYOUTS[layout], self.ld, segments, ALGOS[algo])
+        if segments == 0 and algo == "auto":
+            rc = lib.topk_cols_create(ctypes.byref(self._h), V, C, k, DTYPES[dtype], LAYOUTS[layout], self.ld)
+        else:
+            rc = lib.topk_cols_create_tuned(ctypes.byref(self._h), V, C, k, DTYPES[dtype],
+                                            LAYOUTS[layout], self.ld, segments, ALGOS[algo])
         if rc != TOPK_OK:
             raise TopkError(rc, "topk_cols_create")
 
@@ -114,6 +123,20 @@ class TopkCols:
             raise TopkError(rc, "topk_cols_query")
         names = {v: n for n, v in ALGOS.items()}
         return {"segments": s.value, "blocks": b.value, "workspace_bytes": w.value, "algo": names.get(a.value)}
+
+    def check(self) -> int:
+        """topk_cols_check: synchronizes the device; TOPK_OK, or TOPK_ERR_TIMEOUT
+        when a run's cross-workgroup wait gave up (the workspace is then reset)."""
+        rc = load().topk_cols_check(self._h)
+        if rc not in (TOPK_OK, TOPK_ERR_TIMEOUT):
+            raise TopkError(rc, "topk_cols_check")
+        return rc
+
+    def debug_fail_waits(self, on: bool) -> None:
+        """Tests of the error path only (topk_cols_debug_fail_waits)."""
+        rc = load().topk_cols_debug_fail_waits(self._h, 1 if on else 0)
+        if rc != TOPK_OK:
+            raise TopkError(rc, "topk_cols_debug_fail_waits")
 
     def run_ptr(self, x_ptr: int, values_ptr: int, ids_ptr: int, stream_ptr: int,
                 n_cols: int | None = None, id_map_ptr: int | None = None) -> None:

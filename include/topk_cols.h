@@ -36,7 +36,8 @@ typedef enum {
     TOPK_ERR_INVALID_ARG = -1,  /* an argument is out of range, NULL or misaligned */
     TOPK_ERR_UNSUPPORTED = -2,  /* valid, but beyond this build's limits (k > TOPK_MAX_K, V > TOPK_MAX_V) */
     TOPK_ERR_HIP = -3,          /* a HIP runtime call failed (no device, launch error, ...) */
-    TOPK_ERR_OUT_OF_MEMORY = -4 /* the workspace could not be allocated */
+    TOPK_ERR_OUT_OF_MEMORY = -4, /* the workspace could not be allocated */
+    TOPK_ERR_TIMEOUT = -5       /* reported by topk_cols_check: a run's cross-workgroup wait gave up */
 } topk_status;
 
 typedef enum {
@@ -67,12 +68,14 @@ typedef struct topk_cols *topk_cols_t;
  *     (row-interleaved).  Elements in the padding are never read.
  *
  * The handle owns a small device workspace: one partial list of k 8-byte
- * keys per column and vocabulary segment (C * segments * k keys) and, for the
- * column-contiguous layout, one 128-byte counter line per column, or, for
- * the row-interleaved layout, 16 4-byte bound slots per column that the
- * segments of a column share during a run.  Create
- * allocates it on the current device with hipMalloc, zeroes it and waits for
- * the zeroing to finish; create is not meant for the hot loop.
+ * keys per column and vocabulary segment (C * segments * k keys), an error
+ * word and, for the column-contiguous layout, one 128-byte line per column
+ * holding a counter and the run count modulo 255, or, for the
+ * row-interleaved layout, 16 4-byte bound slots per column that the
+ * segments of a column share during a run.  Create allocates it on the
+ * current device with hipMalloc, zeroes it and waits for the zeroing to
+ * finish; create is not meant for the hot loop.  Every run leaves the
+ * workspace ready for the next one; nothing is reset from the host.
  *
  * On any failure *out is set to NULL, and nothing stays allocated.
  * Returns TOPK_ERR_INVALID_ARG for a bad argument or a NULL out.
@@ -101,11 +104,19 @@ int topk_cols_create(topk_cols_t *out, int64_t V, int64_t C, int32_t k, int32_t 
  * ordered on a single stream: the workspace serves one run at a time.  Use a
  * separate handle for each stream that runs concurrently.
  *
- * Graph capture: a row-interleaved run leaves the workspace as it found it
- * (its second kernel clears what the first one shared), so it may be
- * captured and replayed.  A column-contiguous run tags its keys with a value
- * chosen on the host for each call; a replay would repeat the tag, so those
- * runs must not be captured.
+ * Graph capture: a run's enqueued work depends only on the handle's shape
+ * and the arguments; the state that changes from run to run (the run count
+ * that tags the column-contiguous layout's cross-workgroup lists) lives in
+ * the workspace and is advanced by the kernels.  A run may therefore be
+ * captured into a HIP graph and replayed (each replay is a run: replays
+ * must not overlap each other or other runs on the handle).
+ *
+ * Cross-workgroup wait (column-contiguous layout): each column is merged by
+ * one of its workgroups, which waits, with a bound of tens of milliseconds,
+ * for the others' lists.  The others are running when it starts to wait, so
+ * the bound is never reached in normal operation.  If it were, that
+ * workgroup writes no output for the column and sets the workspace's error
+ * word; topk_cols_check reports it.
  *
  * Returns TOPK_ERR_INVALID_ARG for a NULL or misaligned pointer, or a NULL
  * handle.  Returns TOPK_ERR_HIP when the launch fails.
@@ -131,9 +142,6 @@ int topk_cols_destroy(topk_cols_t h);
  * handle's launch decomposition (segments per column) stays the one chosen
  * at create, and the results are the same as a run on a matrix of n_cols
  * columns.  Ownership, ordering and capture rules are those of topk_cols_run.
- * A column-contiguous run over fewer columns than the last may clear the
- * handle's lists with hipMemsetAsync on the stream (when all 255 run tags
- * are still held by some column's old lists).
  *
  * Returns TOPK_ERR_INVALID_ARG for n_cols < 0 or n_cols > C, and otherwise
  * as topk_cols_run.
@@ -200,6 +208,31 @@ int topk_cols_sample(const void *values, const int32_t *ids, int64_t C, int32_t 
 const char *topk_cols_status_string(int status);
 
 /*
+ * Report whether any run on the handle since the last check had a
+ * cross-workgroup wait give up (see topk_cols_run).  Waits for all work on
+ * the handle's device to finish (hipDeviceSynchronize) and reads the
+ * handle's error word: not meant for the hot loop.
+ *
+ * Returns TOPK_OK when no wait gave up.  Returns TOPK_ERR_TIMEOUT when one
+ * did: the outputs of the runs since the last check are not valid, and the
+ * handle's workspace has been reset (zeroed, synchronously), so later runs
+ * are valid again.  Returns TOPK_ERR_INVALID_ARG for a NULL handle and
+ * TOPK_ERR_HIP when a HIP call fails.
+ */
+int topk_cols_check(topk_cols_t h);
+
+/*
+ * For tests of the error path only: with on != 0, every later column-
+ * contiguous run of the handle (with more than one segment per column) has
+ * its merging workgroups treat every other list as not yet written and give
+ * up after a few re-reads, as if a list never arrived.  Every kernel still
+ * runs to completion.  topk_cols_check then returns TOPK_ERR_TIMEOUT and
+ * resets the workspace.  on = 0 restores normal runs.  Returns
+ * TOPK_ERR_INVALID_ARG for a NULL handle.
+ */
+int topk_cols_debug_fail_waits(topk_cols_t h, int32_t on);
+
+/*
  * Like topk_cols_create, but with the vocabulary-axis split fixed to
  * `segments` workgroups per column (row segments for the interleaved layout)
  * instead of the automatic choice; 0 means automatic.  For tests and tuning:
@@ -215,7 +248,6 @@ int topk_cols_create_with_segments(topk_cols_t *out, int64_t V, int64_t C, int32
 typedef enum {
     TOPK_ALGO_AUTO = 0,       /* chosen from the shape */
     TOPK_ALGO_WORKGROUP = 1,  /* a workgroup per vocabulary segment */
-    TOPK_ALGO_WAVE = 2,       /* a wave per vocabulary segment (4 per workgroup) */
     TOPK_ALGO_ONE_WAVE = 3    /* one wave per column and no vocabulary split: the design that the
                                  "DFlash2" page ("How it works") replaced, kept as a baseline;
                                  never chosen automatically */
@@ -225,9 +257,8 @@ typedef enum {
  * Like topk_cols_create_with_segments, with the kernel family fixed as well
  * (column-contiguous layout; the row-interleaved layout accepts only
  * TOPK_ALGO_AUTO).  For tests and tuning: every family gives the same result.
- * With TOPK_ALGO_WAVE, 4 * segments * k above 2048 returns
- * TOPK_ERR_UNSUPPORTED.  TOPK_ALGO_ONE_WAVE accepts segments 0 or 1 only
- * (else TOPK_ERR_UNSUPPORTED).  An unknown algo returns TOPK_ERR_INVALID_ARG.
+ * TOPK_ALGO_ONE_WAVE accepts segments 0 or 1 only (else
+ * TOPK_ERR_UNSUPPORTED).  An unknown algo returns TOPK_ERR_INVALID_ARG.
  */
 int topk_cols_create_tuned(topk_cols_t *out, int64_t V, int64_t C, int32_t k, int32_t dtype,
                            int32_t layout, int64_t ld, int64_t segments, int32_t algo);

@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_status_strings_cover_every_code(lib):
     for code in (T.TOPK_OK, T.TOPK_ERR_INVALID_ARG, T.TOPK_ERR_UNSUPPORTED, T.TOPK_ERR_HIP,
-                 T.TOPK_ERR_OUT_OF_MEMORY):
+                 T.TOPK_ERR_OUT_OF_MEMORY, T.TOPK_ERR_TIMEOUT):
         s = T.status_string(code)
         assert s and "unknown" not in s
     assert "unknown" in T.status_string(12345)
@@ -100,10 +100,10 @@ def test_tuned_create_checks_its_arguments(lib):
     assert rc == T.TOPK_ERR_UNSUPPORTED and h.value is None
     rc, h = tuned(100, 448, 8, 0, 1, 448, 0, 3)         # ... and column-contiguous only
     assert rc == T.TOPK_ERR_UNSUPPORTED and h.value is None
-    rc, h = tuned(100, 448, 8, 0, 1, 448, 0, 2)         # row-interleaved takes only "auto"
+    rc, h = tuned(100, 448, 8, 0, 1, 448, 0, 1)         # row-interleaved takes only "auto"
     assert rc == T.TOPK_ERR_UNSUPPORTED and h.value is None
-    rc, h = tuned(100000, 56, 64, 0, 0, 100000, 9, 2)   # wave merge: 4*9*64 > 2048 keys
-    assert rc == T.TOPK_ERR_UNSUPPORTED and h.value is None
+    rc, h = tuned(100, 7, 8, 0, 0, 100, 0, 2)           # 2: the removed wave-per-segment family
+    assert rc == T.TOPK_ERR_INVALID_ARG and h.value is None
 
 
 def test_null_out_pointer_refused(lib):
@@ -115,6 +115,8 @@ def test_null_handle_calls(lib):
     assert lib.topk_cols_run(None, 16, 16, 16, None) == T.TOPK_ERR_INVALID_ARG
     assert lib.topk_cols_run_n(None, 1, 16, 16, 16, None) == T.TOPK_ERR_INVALID_ARG
     assert lib.topk_cols_run_mapped(None, 1, 16, 16, 16, 16, None) == T.TOPK_ERR_INVALID_ARG
+    assert lib.topk_cols_check(None) == T.TOPK_ERR_INVALID_ARG
+    assert lib.topk_cols_debug_fail_waits(None, 1) == T.TOPK_ERR_INVALID_ARG
 
 
 def test_sample_checks_its_arguments_before_any_launch(lib):

@@ -162,3 +162,22 @@ def test_graph_replay(gpu):
             ov, oi = ref[i]
             bad = np.flatnonzero((gi != oi).any(axis=1) | (bits(gv) != bits(ov)).any(axis=1))
             assert bad.size == 0, f"replay {rep}: {bad.size} columns differ, first {bad[0]}"
+
+
+@pytest.mark.parametrize("kind,dtype,V,segments", [
+    ("asc", W.BF16, 32639, 16),      # the longest strictly increasing bf16 column
+    ("asc", W.F32, 248046, 0),
+    ("equal", W.BF16, 248046, 0),
+    ("desc", W.F32, 248046, 0),
+    ("desc", W.BF16, 32639, 16),
+])
+def test_overflow_rebuild_with_shared_bound(gpu, kind, dtype, V, segments):
+    """Long columns with several passes per segment and at least k segments,
+    so the shared bound fills while columns overflow their buffers and are
+    rebuilt: ascending columns overflow in every pass, all-equal ones end on
+    the exact path, descending ones stop passing the filter at once."""
+    C, k = 64, 16
+    x = W.random_matrix(4321, V, C, dtype, W.ROW, kind=kind)
+    print(f"[parity-row] overflow and rebuild, {kind} {dtype} V={V} C={C} k={k} segments={segments}", flush=True)
+    assert_parity(gpu, x, V, C, k, dtype, W.ROW, C, segments=segments,
+                  label=f"row {kind} {dtype} V={V} segments={segments}")
