@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libtopk_cols.so")
 SOURCES = [os.path.join(CSRC, n) for n in ("topk_col.hip", "topk_row.hip", "topk_onewave.hip",
-                                            "topk_sample.hip", "topk_cols_api.cpp")]
+                                            "topk_sample.hip", "topk_noalloc.hip", "topk_cols_api.cpp")]
 OBJDIR = os.path.join(ROOT, "_build")
 # Per-source flags.  The column kernel takes its ticket before ranking and
 # publishing its list and reads the reply afterwards; the compiler's atomic

@@ -260,7 +260,19 @@ int topk_cols_run_mapped(topk_cols_t h, int64_t n_cols, const void* logits, cons
 }
 
 int topk_cols_check(topk_cols_t h) {
-    if (!h) return TOPK_ERR_INVALID_ARG;
+    if (!h) {
+        // the no-allocation entry point's workspace on the current device
+        void* ws = nullptr;
+        size_t bytes = 0;
+        const int st = topk::noalloc_workspace(&ws, &bytes);
+        if (st != TOPK_OK) return st;
+        uint32_t err = 0;
+        if (hipDeviceSynchronize() != hipSuccess || hipMemcpy(&err, ws, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess)
+            return TOPK_ERR_HIP;
+        if (err == 0) return TOPK_OK;
+        if (hipMemset(ws, 0, bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) return TOPK_ERR_HIP;
+        return TOPK_ERR_TIMEOUT;
+    }
     int prev = 0;
     if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(h->device) != hipSuccess) return TOPK_ERR_HIP;
     int status = TOPK_OK;

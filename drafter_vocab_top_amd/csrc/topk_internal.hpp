@@ -122,6 +122,10 @@ hipError_t launch_plan(const Plan& plan, void* ws, int64_t n_cols, const void* l
                        void* out_values, int32_t* out_ids, uint32_t spin_limit, uint32_t fail_waits,
                        uint32_t clear_lists, hipStream_t stream);
 
+// The no-allocation entry point's workspace on the current device (a
+// static array): its device address and size.
+int noalloc_workspace(void** ptr, size_t* bytes);
+
 // Re-reads of a list slot before a merging workgroup gives up (each costs a
 // device round trip of about a microsecond: tens of milliseconds in all).
 constexpr uint32_t kDefaultSpinLimit = 1u << 16;

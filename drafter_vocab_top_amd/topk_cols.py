@@ -34,7 +34,7 @@ LAYOUTS = {"col": 0, "row": 1}
 EXPORTED = ("topk_cols_create", "topk_cols_create_with_segments", "topk_cols_create_tuned",
             "topk_cols_run", "topk_cols_run_n", "topk_cols_run_mapped", "topk_cols_sample",
             "topk_cols_destroy", "topk_cols_status_string", "topk_cols_query", "topk_cols_check",
-            "topk_cols_debug_fail_waits")
+            "topk_cols_debug_fail_waits", "topk_cols_run_noalloc")
 # kernel families of the column-contiguous layout ("one_wave": the baseline
 # design with one wave per column and no vocabulary split)
 ALGOS = {"auto": 0, "workgroup": 1, "one_wave": 3}
@@ -83,6 +83,8 @@ def load(path: str = LIBRARY):
     lib.topk_cols_check.restype = ctypes.c_int
     lib.topk_cols_debug_fail_waits.argtypes = [p, i32]
     lib.topk_cols_debug_fail_waits.restype = ctypes.c_int
+    lib.topk_cols_run_noalloc.argtypes = [i64, i64, i32, i32, i32, i64, p, p, p, p]
+    lib.topk_cols_run_noalloc.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -241,6 +243,34 @@ def sample(values, ids, temperature: float = 1.0, top_p: float = 0.95, seed: int
     if rc != TOPK_OK:
         raise TopkError(rc, "topk_cols_sample")
     return out_ids, out_pos
+
+
+def run_noalloc(x, V: int, C: int, k: int, dtype: str = "bf16", layout: str = "col", ld=None,
+                values=None, ids=None, stream=None):
+    """topk_cols_run_noalloc: one run with no handle and no device allocation
+    by the library (the outputs are allocated here when not given).  Returns
+    (values, ids) shaped (C, k); enqueued on the current stream by default."""
+    import torch
+    if dtype not in DTYPES or layout not in LAYOUTS:
+        raise ValueError(f"dtype must be one of {list(DTYPES)}, layout one of {list(LAYOUTS)}")
+    ld = ld if ld is not None else (V if layout == "col" else C)
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous GPU tensor")
+    need = (C - 1) * ld + V if layout == "col" else (V - 1) * ld + C
+    if x.numel() < need or x.element_size() != (2 if dtype == "bf16" else 4):
+        raise ValueError("x does not hold the matrix described")
+    if values is None:
+        values = torch.empty((C, k), dtype=x.dtype, device=x.device)
+    if ids is None:
+        ids = torch.empty((C, k), dtype=torch.int32, device=x.device)
+    if values.numel() < C * k or ids.numel() < C * k:
+        raise ValueError("output buffers are too small")
+    s = stream if stream is not None else torch.cuda.current_stream(x.device)
+    rc = load().topk_cols_run_noalloc(V, C, k, DTYPES[dtype], LAYOUTS[layout], ld, x.data_ptr(), values.data_ptr(),
+                                      ids.data_ptr(), s.cuda_stream)
+    if rc != TOPK_OK:
+        raise TopkError(rc, "topk_cols_run_noalloc")
+    return values, ids
 
 
 def topk_cols(x, V: int, C: int, k: int, dtype: str = "bf16", layout: str = "col", ld=None):

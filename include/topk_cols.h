@@ -112,11 +112,12 @@ int topk_cols_create(topk_cols_t *out, int64_t V, int64_t C, int32_t k, int32_t 
  * must not overlap each other or other runs on the handle).
  *
  * Cross-workgroup wait (column-contiguous layout): each column is merged by
- * one of its workgroups, which waits, with a bound of tens of milliseconds,
- * for the others' lists.  The others are running when it starts to wait, so
- * the bound is never reached in normal operation.  If it were, that
- * workgroup writes no output for the column and sets the workspace's error
- * word; topk_cols_check reports it.
+ * the last of its workgroups to finish, which reads the others' lists and
+ * waits, with a bound of tens of milliseconds, for any that has not landed
+ * yet.  Every list was stored before its workgroup finished, so the wait
+ * only covers stores still in flight and the bound is never reached in
+ * normal operation.  If it were, that workgroup writes no output for the
+ * column and sets the workspace's error word; topk_cols_check reports it.
  *
  * Returns TOPK_ERR_INVALID_ARG for a NULL or misaligned pointer, or a NULL
  * handle.  Returns TOPK_ERR_HIP when the launch fails.
@@ -208,16 +209,48 @@ int topk_cols_sample(const void *values, const int32_t *ids, int64_t C, int32_t 
 const char *topk_cols_status_string(int status);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the run of
+ * topk_cols_run for the shape (V, C, k, dtype, layout, ld) of
+ * topk_cols_create, with no handle.  Nothing is allocated: the workspace is
+ * a static array of 8 MiB that each GPU the library runs on holds until the
+ * process ends.  The first call on a device looks the array's address up
+ * (hipGetSymbolAddress); later calls only launch kernels.
+ *
+ * Arguments as for topk_cols_create and topk_cols_run (all pointers device
+ * pointers owned by the caller).  The launch decomposition is the one
+ * topk_cols_create would choose; results are identical to a handle's.
+ * Asynchronous on stream; no synchronization, no allocation.
+ *
+ * Every call on a GPU shares that GPU's array, which keeps what the last
+ * call left: each call that completes leaves the parts that must start at
+ * zero at zero, so calls of any shape and layout may follow each other on
+ * one stream, or be captured and replayed.  Calls that overlap on one GPU
+ * (unordered streams, overlapping replays) race: order them.  A
+ * cross-workgroup wait that gives up (never in normal operation) leaves an
+ * error in the array; topk_cols_check(NULL) reports it and clears the array.
+ *
+ * Returns the errors of topk_cols_create for a bad shape, and
+ * TOPK_ERR_UNSUPPORTED when C > 4096 or the shape's workspace exceeds the
+ * array (for example 248,046 x 448 bf16 rows with k = 16 needs 4.2 MiB and
+ * fits); TOPK_ERR_INVALID_ARG for a NULL or misaligned pointer;
+ * TOPK_ERR_HIP when there is no device or the launch fails.
+ */
+int topk_cols_run_noalloc(int64_t V, int64_t C, int32_t k, int32_t dtype, int32_t layout, int64_t ld,
+                          const void *logits, void *out_values, int32_t *out_ids, hipStream_t stream);
+
+/*
  * Report whether any run on the handle since the last check had a
  * cross-workgroup wait give up (see topk_cols_run).  Waits for all work on
  * the handle's device to finish (hipDeviceSynchronize) and reads the
- * handle's error word: not meant for the hot loop.
+ * handle's error word: not meant for the hot loop.  With h = NULL it checks
+ * the workspace of topk_cols_run_noalloc on the current device instead.
  *
  * Returns TOPK_OK when no wait gave up.  Returns TOPK_ERR_TIMEOUT when one
  * did: the outputs of the runs since the last check are not valid, and the
- * handle's workspace has been reset (zeroed, synchronously), so later runs
- * are valid again.  Returns TOPK_ERR_INVALID_ARG for a NULL handle and
- * TOPK_ERR_HIP when a HIP call fails.
+ * workspace has been reset (zeroed, synchronously), so later runs are valid
+ * again.  Returns TOPK_ERR_HIP when a HIP call fails (for h = NULL: also
+ * when there is no device).
  */
 int topk_cols_check(topk_cols_t h);
 

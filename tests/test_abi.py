@@ -115,8 +115,12 @@ def test_null_handle_calls(lib):
     assert lib.topk_cols_run(None, 16, 16, 16, None) == T.TOPK_ERR_INVALID_ARG
     assert lib.topk_cols_run_n(None, 1, 16, 16, 16, None) == T.TOPK_ERR_INVALID_ARG
     assert lib.topk_cols_run_mapped(None, 1, 16, 16, 16, 16, None) == T.TOPK_ERR_INVALID_ARG
-    assert lib.topk_cols_check(None) == T.TOPK_ERR_INVALID_ARG
     assert lib.topk_cols_debug_fail_waits(None, 1) == T.TOPK_ERR_INVALID_ARG
+    for args in ((None, 16, 16), (16, None, 16), (16, 16, None)):      # NULL logits, values, ids
+        assert lib.topk_cols_run_noalloc(1000, 7, 8, 0, 0, 1000, *args, None) == T.TOPK_ERR_INVALID_ARG
+    assert lib.topk_cols_run_noalloc(1000, 7, 8, 0, 0, 1000, 17, 16, 16, None) == T.TOPK_ERR_INVALID_ARG  # misaligned
+    assert lib.topk_cols_run_noalloc(1000, 7, 65, 0, 0, 1000, 16, 16, 16, None) == T.TOPK_ERR_UNSUPPORTED
+    assert lib.topk_cols_run_noalloc(1000, 7, 8, 0, 0, 999, 16, 16, 16, None) == T.TOPK_ERR_INVALID_ARG  # ld < V
 
 
 def test_sample_checks_its_arguments_before_any_launch(lib):
@@ -150,3 +154,6 @@ def test_valid_create_without_a_device_fails_cleanly(lib):
     rc, h = _create(lib, 248046, 7, 8, 0, 0, 248046)
     assert rc == T.TOPK_ERR_HIP
     assert h.value is None
+    # the no-allocation entry point and its check need a device as well
+    assert lib.topk_cols_run_noalloc(248046, 7, 8, 0, 0, 248046, 16, 16, 16, None) == T.TOPK_ERR_HIP
+    assert lib.topk_cols_check(None) == T.TOPK_ERR_HIP
