@@ -111,6 +111,9 @@ def time_config(torch, T, w, steps, warmup, per_call_steps=None, warm=True, algo
     hh = h._h
     R, ptrs = rot.R, rot.ptrs
 
+    # the copies are read in one sequence: warm-up, timed region, per-call
+    # region; a copy is read again only after all R copies (>= 1 GiB) have
+    # been read since, so no timed call finds its input in a cache
     for s in range(warmup):
         run(hh, ptrs[s % R], pv, pi, sp)
     torch.cuda.synchronize()
@@ -119,7 +122,7 @@ def time_config(torch, T, w, steps, warmup, per_call_steps=None, warm=True, algo
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_host = time.perf_counter()
     e0.record(stream)
-    for s in range(steps):
+    for s in range(warmup, warmup + steps):
         run(hh, ptrs[s % R], pv, pi, sp)
     e1.record(stream)
     host_us = (time.perf_counter() - t_host) * 1e6 / steps
@@ -130,9 +133,10 @@ def time_config(torch, T, w, steps, warmup, per_call_steps=None, warm=True, algo
     n_pc = per_call_steps or steps
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_pc)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_pc)]
+    first = warmup + steps
     for s in range(n_pc):
         starts[s].record(stream)
-        run(hh, ptrs[s % R], pv, pi, sp)
+        run(hh, ptrs[(first + s) % R], pv, pi, sp)
         ends[s].record(stream)
     torch.cuda.synchronize()
     per_call = sorted(starts[s].elapsed_time(ends[s]) * 1000.0 for s in range(n_pc))
@@ -145,6 +149,8 @@ def time_config(torch, T, w, steps, warmup, per_call_steps=None, warm=True, algo
         "per_call_p10_us": per_call[len(per_call) // 10],
         "per_call_p90_us": per_call[(9 * len(per_call)) // 10],
         "rotation_copies": R,
+        "rotation": f"warm-up reads copies 0..{warmup - 1}, the timed calls copies {warmup % R}.. "
+                    f"(mod {R}), the per-call region after them",
         "decomposition": h.query(),
     }
     if warm:
@@ -159,7 +165,7 @@ def time_config(torch, T, w, steps, warmup, per_call_steps=None, warm=True, algo
         res["warm_us_per_round"] = e0.elapsed_time(e1) * 1000.0 / steps
     # the timed outputs must be the right answer: compare the last call's
     # result with a fresh run on the same input (cheap self-check)
-    run(hh, ptrs[(n_pc - 1) % R], pv, pi, sp)
+    run(hh, ptrs[(first + n_pc - 1) % R], pv, pi, sp)
     torch.cuda.synchronize()
     res["_last"] = (vals.cpu().numpy(), ids.cpu().numpy())
     h.close()
@@ -232,6 +238,30 @@ def time_sampler(torch, T, w, steps=1000, warmup=20):
     return e0.elapsed_time(e1) * 1000.0 / steps
 
 
+def launch_floor_eager(torch, steps, warmup=50):
+    """Back-to-back launches of an empty kernel (one workgroup), each its own
+    eager ctypes call on the current stream between one event pair: the same
+    protocol as the top-k's amortized figure."""
+    import ctypes
+    from drafter_vocab_top_amd import build as B
+    lib = ctypes.CDLL(B.STREAM_LIBRARY)
+    lib.stream_read_empty.argtypes = [ctypes.c_void_p]
+    lib.stream_read_empty.restype = ctypes.c_int
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    for _ in range(warmup):
+        if lib.stream_read_empty(sp) != 0:
+            raise RuntimeError("stream_read_empty failed")
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        lib.stream_read_empty(sp)
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) * 1000.0 / steps
+
+
 def launch_floor(torch, steps):
     """Back-to-back empty-kernel launches (torch's sleep kernel with 0 cycles),
     captured in a graph so host overhead does not count."""
@@ -258,11 +288,12 @@ def launch_floor(torch, steps):
     return e0.elapsed_time(e1) * 1000.0 / (reps * 200)
 
 
-def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0):
-    """The oracle, as it stands, on whole rounds of workload w on host cores."""
+def cpu_baseline(w, threads=None, min_seconds=10.0, max_seconds=30.0):
+    """The oracle, as it stands, on whole rounds of workload w on host cores
+    (threads over columns; default min(C, cores))."""
     import oracle
     cores = len(os.sched_getaffinity(0))
-    threads = max(1, min(w.C, cores))
+    threads = threads or max(1, min(w.C, cores))
     odt = oracle.BF16 if w.dtype == "bf16" else oracle.F32
     oly = oracle.COL_CONTIG if w.layout == "col" else oracle.ROW_INTERLEAVED
     oracle.topk_cols(w.x, w.V, w.C, w.k, odt, oly, w.ld, nthreads=threads)  # load + warm
@@ -292,6 +323,19 @@ def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0):
         "host_cores_available": cores,
         "cpu_model": cpu,
     }, res
+
+
+def device_clocks():
+    """The GPU's clock lines as rocm-smi prints them (a child process; None
+    when rocm-smi is not there or fails)."""
+    import subprocess
+    try:
+        p = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    lines = [ln.strip() for ln in p.stdout.splitlines()
+             if re.search(r"\b(sclk|mclk|fclk|socclk)\b", ln) and "level" in ln]
+    return lines or None
 
 
 def device_info(torch):
@@ -370,6 +414,86 @@ def summarize_counters(fetch_dir, write_dir, config_n, out_path=None):
     return out
 
 
+def trace_path(w, config_n, ext):
+    kind = "col" if w.layout == "col" else "row"
+    return os.path.join(ROOT, "profiles", f"topk_{kind}_kernel_cfg{config_n}_ktrace.{ext}")
+
+
+def summarize_trace(trace_dir, config_n, label="", out_dir=None):
+    """Per-kernel durations of the top-k kernels in the run_kernel_trace.csv
+    of a 'rocprofv3 --kernel-trace' run of '--profile N': written as
+    profiles/topk_*_kernel_cfgN_ktrace.json (with the sources' digest) and a
+    markdown table beside it."""
+    import csv
+    from drafter_vocab_top_amd import workloads as W
+    w = W.config(config_n)
+    durs, res = {}, {}
+    for root, _, files in os.walk(trace_dir):
+        for fn in files:
+            if not fn.endswith("kernel_trace.csv"):
+                continue
+            with open(os.path.join(root, fn), newline="") as f:
+                for rec in csv.DictReader(f):
+                    m = re.search(r"topk_\w+(<[^()]*>)?", rec.get("Kernel_Name", ""))
+                    if not m:
+                        continue
+                    name = m.group(0)
+                    durs.setdefault(name, []).append(
+                        (int(rec["End_Timestamp"]) - int(rec["Start_Timestamp"])) / 1000.0)
+                    res[name] = {"vgpr": int(rec["VGPR_Count"]), "accum_vgpr": int(rec["Accum_VGPR_Count"]),
+                                 "sgpr": int(rec["SGPR_Count"]), "lds_bytes": int(rec["LDS_Block_Size"]),
+                                 "scratch_bytes": int(rec["Scratch_Size"]),
+                                 "workgroup": int(rec["Workgroup_Size_X"]),
+                                 "grid": int(rec["Grid_Size_X"])}
+    if not durs:
+        raise SystemExit(f"no top-k dispatches under {trace_dir}")
+    cmd = (f"rocprofv3 --kernel-trace --stats -u usec -f csv -d {trace_dir} -o run -- "
+           f"python3 bench.py --profile {config_n} --steps 200 --warmup 20")
+    out = {"workload": w.name, "kernel_sources_digest": kernel_sources_digest(w.layout),
+           "commands": [cmd, f"python3 bench.py --summarize-trace {trace_dir} {config_n}"], "kernels": {}}
+    for name, d in durs.items():
+        d = sorted(d)
+        out["kernels"][name] = dict(calls=len(d), mean_us=statistics.fmean(d), median_us=d[len(d) // 2],
+                                    p10_us=d[len(d) // 10], p90_us=d[(9 * len(d)) // 10], min_us=d[0],
+                                    max_us=d[-1], **res[name])
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    base = os.path.basename(trace_path(w, config_n, "json"))
+    with open(os.path.join(out_dir, base), "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    lines = [f"# Kernel trace: {w.name}{(' ' + label) if label else ''}", "",
+             "Commands (from the repository root, on one MI355X; `cd /tmp && export TMPDIR=/tmp` first):", ""]
+    lines += [f"    {c}" for c in out["commands"]]
+    lines += ["", f"Sources digest: `{out['kernel_sources_digest']}`.  `--profile {config_n}` makes 421 calls "
+              "on rotating cold inputs (20 warm-up, 200 back to back, 200 with an event pair each, 1 check), "
+              "then a plain 256 MiB copy five times.", "",
+              "| kernel | calls | mean (us) | median (us) | p10 | p90 | min | max | VGPR | SGPR | LDS (B) | scratch | grid x wg |",
+              "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for name, k in out["kernels"].items():
+        lines.append(f"| `{name}` | {k['calls']} | {k['mean_us']:.3f} | {k['median_us']:.3f} | {k['p10_us']:.3f} | "
+                     f"{k['p90_us']:.3f} | {k['min_us']:.3f} | {k['max_us']:.3f} | {k['vgpr']} | {k['sgpr']} | "
+                     f"{k['lds_bytes']} | {k['scratch_bytes']} | {k['grid'] // max(1, k['workgroup'])} x "
+                     f"{k['workgroup']} |")
+    with open(os.path.join(out_dir, base[:-5] + ".md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps(out, indent=1))
+    return out
+
+
+def trace_record(digest, w, config_n):
+    """Kernel-only durations from a committed trace summary whose digest
+    matches the sources (else None)."""
+    path = trace_path(w, config_n, "json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sources_digest") != digest:
+        return None
+    return {name: {"median_us": k["median_us"], "mean_us": k["mean_us"], "calls": k["calls"]}
+            for name, k in rec["kernels"].items()}
+
+
 def traffic_record(digest, w, config_n):
     path = traffic_path(w, config_n)
     if not os.path.exists(path):
@@ -399,7 +523,14 @@ def main():
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "N"),
                     help="turn the counter_collection.csv files of a FETCH_SIZE and a WRITE_SIZE "
                          "rocprofv3 run of '--profile N' into profiles/topk_*_cfgN_traffic.json")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "N"),
+                    help="turn the kernel_trace.csv of a 'rocprofv3 --kernel-trace' run of '--profile N' "
+                         "into profiles/topk_*_kernel_cfgN_ktrace.{json,md}")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace[0], int(args.summarize_trace[1]))
+        return
 
     if args.summarize_counters:
         fetch_dir, write_dir, n = args.summarize_counters
@@ -438,7 +569,8 @@ def main():
     log(f"device: {device_info(torch)}")
     per_config = {}
     floor_us = launch_floor(torch, 2000)
-    log(f"launch floor (empty kernel, graph): {floor_us:.3f} us")
+    floor_eager_us = launch_floor_eager(torch, 2000)
+    log(f"launch floor (empty kernel): graph {floor_us:.3f} us, eager ctypes launches {floor_eager_us:.3f} us")
     wanted = sorted(set(int(c) for c in args.configs.split(",") if c) | {HEADLINE})
     headline = None
     for n in wanted:
@@ -508,6 +640,7 @@ def main():
     w, r = headline
     digest = kernel_sources_digest(w.layout)
     traffic = traffic_record(digest, w, HEADLINE)
+    trace = trace_record(digest, w, HEADLINE)
     b = algorithmic_bytes(w)
     achieved = b / (r["us_per_round"] * 1e3)
     cpu = None
@@ -515,6 +648,11 @@ def main():
         log("timing the CPU oracle (cpu_baseline) ...")
         cpu, _ = cpu_baseline(w)
         log(f"  oracle: {cpu['value']:.0f} us/round on {cpu['cores']} threads")
+        one, _ = cpu_baseline(w, threads=1)
+        cpu["single_thread"] = {k: one[k] for k in ("value", "unit", "cores", "sample")}
+        log(f"  oracle: {one['value']:.0f} us/round on 1 thread")
+    clocks = device_clocks()
+    log(f"clocks after the timed runs: {clocks}")
     out = {
         "metric": METRIC,
         "value": round(r["us_per_round"], 3),
@@ -533,13 +671,15 @@ def main():
                    "blocks": r["decomposition"]["blocks"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
-                     "algorithmic_bytes": b, "kernel_mean_us": r["us_per_round"],
-                     "kernel": "topk_col_kernel" if w.layout == "col" else "topk_row_scan + topk_row_merge"},
+                     "algorithmic_bytes": b, "event_us_per_launch": r["us_per_round"],
+                     "kernel": "topk_col_kernel" if w.layout == "col" else "topk_row_scan + topk_row_merge",
+                     "kernel_trace": trace},
         "cpu_baseline": cpu,
         "launch_floor_us": floor_us,
+        "launch_floor_eager_us": floor_eager_us,
         "per_config": per_config,
         "kernel_sources_digest": digest,
-        "device": device_info(torch),
+        "device": dict(device_info(torch), clocks_after_timing=clocks),
     }
     print(json.dumps(out), flush=True)
 

@@ -17,6 +17,9 @@
 //     blocks: workgroups, 1 .. 65,536 (each reads a contiguous chunk);
 //     sink: device, one uint32 that the kernel may write; returns 0, -1 for
 //     a bad argument, -3 when the launch fails.
+//   int stream_read_empty(hipStream_t stream)
+//     launches one workgroup of an empty kernel: the launch floor under the
+//     same eager launches as the top-k; returns 0, -3 when the launch fails.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -54,7 +57,14 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* x, i
     if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
+__global__ __launch_bounds__(64) void empty_kernel() {}
+
 }  // namespace
+
+extern "C" int stream_read_empty(hipStream_t stream) {
+    hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, stream);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+}
 
 extern "C" int stream_read_run(const void* x, int64_t bytes, int64_t blocks, uint32_t* sink, hipStream_t stream) {
     if (!x || !sink || bytes < 16 || bytes % 16 != 0 || ((uintptr_t)x % 16) != 0) return -1;

@@ -223,7 +223,7 @@ __device__ __forceinline__ bool merge_lists(const ColArgs& a, ColShared& sh, con
 // Selection by wave 0 of the column's last workgroup when the S*k published
 // keys fit 16 per lane (coalesced device-scope loads): the k-th largest lane
 // maximum is the threshold, the keys at or above it are ranked (through
-// scalar broadcasts when at most 64), and out(position, key) writes each of
+// 16-byte LDS broadcasts when at most 64), and out(position, key) writes each of
 // the top k.
 template <class DT, class Out>
 __device__ __forceinline__ bool merge_lists_wave(const ColArgs& a, ColShared& sh, const uint64_t* parts,
@@ -267,8 +267,11 @@ __device__ __forceinline__ bool merge_lists_wave(const ColArgs& a, ColShared& sh
         cnt = wave_append(sh.cand, cnt, kBlockCap, valid && key_order(key) >= T, key);
     });
     if (cnt <= 64u) {
-        const uint64_t key = lane < cnt ? sh.cand[lane] : 0ull;
-        const uint32_t r = wave_rank_of(key, cnt);
+        const uint32_t n8 = (cnt + 7u) & ~7u;
+        uint64_t key = 0;
+        if (lane < cnt) key = sh.cand[lane];
+        else if (lane < n8) sh.cand[lane] = 0;  // padding for the rank
+        const uint32_t r = lds_rank_of(sh.cand, n8, key);
         if (lane < cnt && r < k) out(r, key);
         return true;
     }
@@ -309,13 +312,14 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
     const uint32_t vb = nvec * s / S, ve = nvec * (s + 1) / S;
     const u32x4* vec = reinterpret_cast<const u32x4*>(col + head);
 
-    uint64_t edge = 0;  // this lane's edge element (wave 0 only), or 0
-    {
-        uint32_t row = 0xFFFFFFFFu;
-        if (s == 0 && tid < head) row = tid;
-        if (s == S - 1 && tid >= 32 && tid - 32 < V - tail0) row = tail0 + (tid - 32);
-        if (row != 0xFFFFFFFFu) edge = make_key(DT::order(col[row]), row, 0u);  // tagged in pass 0
-    }
+    // This lane's edge element (wave 0 only): its row, or all ones, and its
+    // raw bits.  The load is issued here and its value first used in pass 0,
+    // after the pass's own loads, so that nothing waits for it alone.
+    uint32_t edge_row = 0xFFFFFFFFu;
+    if (s == 0 && tid < head) edge_row = tid;
+    if (s == S - 1 && tid >= 32 && tid - 32 < V - tail0) edge_row = tail0 + (tid - 32);
+    uint32_t edge_raw = 0;
+    if (edge_row != 0xFFFFFFFFu) edge_raw = (uint32_t)col[edge_row];
     if (tid == 0) {
         sh.ncand = 0;
         sh.overflow = 0;
@@ -344,11 +348,14 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
         uint32_t rep;
         bool neg_nan;
         lane_stats<DT, NV>(d, vmax, rep, neg_nan);
+        uint64_t ex = 0;
         if (p == 0) {
             epoch = (uint32_t)__builtin_amdgcn_readfirstlane((int)epoch_v);
             tag = epoch + 1u;
+            // keeps the edge value's first use (and its wait) here
+            asm volatile("" : "+v"(edge_raw));
+            if (edge_row != 0xFFFFFFFFu) ex = make_key(DT::order((storage)edge_raw), edge_row, tag);
         }
-        const uint64_t ex = p == 0 && edge != 0 ? edge | tag : 0;
         if (ex) rep = max_u32(rep, key_order(ex));
         // Each wave's k-th largest lane maximum bounds the workgroup's k-th
         // largest element from below, so the largest of the four does too.
@@ -484,8 +491,11 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
         uint32_t old = 0;
         if (lane == 0) old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (n_last <= 64u) {
-            const uint64_t key = lane < n_last ? sh.cand[lane] : 0ull;
-            const uint32_t r = wave_rank_of(key, n_last);
+            const uint32_t n8 = (n_last + 7u) & ~7u;
+            uint64_t key = 0;
+            if (lane < n_last) key = sh.cand[lane];
+            else if (lane < n8) sh.cand[lane] = 0;  // padding for the rank
+            const uint32_t r = lds_rank_of(sh.cand, n8, key);
             if (lane < n_last && r < k)
                 __hip_atomic_store(&dst[r], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         } else {

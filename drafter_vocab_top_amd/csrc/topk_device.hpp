@@ -213,27 +213,24 @@ __device__ __forceinline__ uint32_t rank_select(const uint64_t* keys, uint32_t n
     return min_u32(n, k);
 }
 
-// Rank of each lane's key among the keys of lanes 0..n-1 (n <= 64,
-// wave-uniform): the number of them that are larger.  Keys are broadcast one
-// lane at a time through scalar registers, so there is no LDS traffic; four
-// independent chains per step hide the scalar-read latency.  Lanes at or
-// past n get a rank as well; callers ignore it.
-__device__ __forceinline__ uint32_t wave_rank_of(uint64_t key, uint32_t n) {
-    const int hi = (int)(uint32_t)(key >> 32), lo = (int)(uint32_t)key;
-    auto lane_key = [&](uint32_t j) {
-        return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(hi, (int)j) << 32) |
-               (uint32_t)__builtin_amdgcn_readlane(lo, (int)j);
-    };
-    uint32_t r0 = 0, r1 = 0, r2 = 0, r3 = 0;
-    uint32_t j = 0;
-    for (; j + 4 <= n; j += 4) {
-        r0 += lane_key(j) > key ? 1u : 0u;
-        r1 += lane_key(j + 1) > key ? 1u : 0u;
-        r2 += lane_key(j + 2) > key ? 1u : 0u;
-        r3 += lane_key(j + 3) > key ? 1u : 0u;
+// Rank of each lane's key among the n <= 64 distinct keys in LDS, keys[0..n8)
+// with n8 = n rounded up to 8 and the slots past n holding 0 (below every
+// key): the number of them that are larger.  All lanes read the same 16 bytes
+// at a time (a broadcast), and the eight comparisons of a step are
+// independent of each other, so the cost is a few LDS reads and compares per
+// eight keys rather than a dependent chain per key.  Lanes whose key is not
+// one of the n get a rank as well; callers ignore it.
+__device__ __forceinline__ uint32_t lds_rank_of(const uint64_t* keys, uint32_t n8, uint64_t key) {
+    uint32_t r0 = 0, r1 = 0;
+    for (uint32_t j = 0; j < n8; j += 8) {
+        const u64x2 q0 = *reinterpret_cast<const u64x2*>(keys + j);
+        const u64x2 q1 = *reinterpret_cast<const u64x2*>(keys + j + 2);
+        const u64x2 q2 = *reinterpret_cast<const u64x2*>(keys + j + 4);
+        const u64x2 q3 = *reinterpret_cast<const u64x2*>(keys + j + 6);
+        r0 += (uint32_t)(q0.x > key) + (uint32_t)(q0.y > key) + (uint32_t)(q1.x > key) + (uint32_t)(q1.y > key);
+        r1 += (uint32_t)(q2.x > key) + (uint32_t)(q2.y > key) + (uint32_t)(q3.x > key) + (uint32_t)(q3.y > key);
     }
-    for (; j < n; ++j) r0 += lane_key(j) > key ? 1u : 0u;
-    return r0 + r1 + r2 + r3;
+    return r0 + r1;
 }
 
 // Rank selection by one wave (see rank_select).
