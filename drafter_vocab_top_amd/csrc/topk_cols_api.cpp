@@ -23,8 +23,6 @@ namespace topk {
 namespace {
 
 constexpr int64_t kBlockThreads = 256;
-// Scan workgroups the row-interleaved launch aims for per CU.
-constexpr int64_t kTargetBlocksPerCU = 2;
 // Do not split a column into segments smaller than this many vectors.
 constexpr int64_t kMinVecsPerSegment = 64;
 
@@ -49,11 +47,13 @@ int64_t choose_col_segments(int64_t V, int64_t C, int dtype, int cu_count) {
     return s < 1 ? 1 : s;
 }
 
-// Row-interleaved: tiles of 128 bytes of a row; row segments so that about
-// kTargetBlocksPerCU workgroups run per CU, each segment at least one
-// 32-row step, and the merge input S*k within its limit.
+// Row-interleaved: tiles of 128 bytes of a row; row segments so that as
+// many workgroups run as fit at once (three per CU for k <= kRowSmallK, else
+// two), each segment at least one 32-row step, and the merge input S*k
+// within its limit.
 int64_t choose_row_segments(int64_t V, int64_t tiles, int32_t k, int cu_count) {
-    int64_t s = (int64_t)cu_count * kTargetBlocksPerCU / tiles;  // no partial second wave
+    const int64_t per_cu = k <= kRowSmallK ? 3 : 2;
+    int64_t s = (int64_t)cu_count * per_cu / tiles;  // no partial last wave
     const int64_t most_rows = V / 32;
     if (s > most_rows) s = most_rows;
     const int64_t merge_cap = kRowMaxMergeKeys / k;

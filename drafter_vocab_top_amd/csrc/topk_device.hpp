@@ -165,9 +165,11 @@ __device__ __forceinline__ uint32_t lanes_below(unsigned long long mask) {
 // Wave-uniform append: every lane calls it; the lanes with `has` write their
 // key to buf[cnt + (number of such lanes below)], positions at or past `cap`
 // are dropped.  Returns the new count (which may exceed cap: overflow).
+// A call in which no lane appends costs a ballot and a scalar branch.
 template <class KeyT>
 __device__ __forceinline__ uint32_t wave_append(KeyT* buf, uint32_t cnt, uint32_t cap, bool has, KeyT key) {
     const unsigned long long m = __ballot(has);
+    if (m == 0ull) return cnt;  // wave-uniform
     if (has) {
         const uint32_t pos = cnt + lanes_below(m);
         if (pos < cap) buf[pos] = key;

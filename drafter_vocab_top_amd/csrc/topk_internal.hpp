@@ -70,6 +70,9 @@ struct RowArgs {
 };
 
 constexpr int kRowMaxMergeKeys = 2048;
+// Row scans with k <= kRowSmallK keep a smaller candidate area and run three
+// workgroups per CU; larger k, two.
+constexpr int kRowSmallK = 16;
 constexpr int kRowBoundSlots = 16;
 
 // One sampled draft per column from its top-k list (values sorted largest

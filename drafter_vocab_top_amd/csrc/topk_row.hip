@@ -74,7 +74,6 @@ constexpr int kRowQueue = 128;                          // queued row vectors pe
 // Candidate buffer per column: CAP keys.  A trim leaves about k of them and
 // is due above max(2k, 24), so a pass may add at least CAP - max(2k, 24)
 // (32 or more) before the buffer overflows.
-constexpr int kRowSmallK = 16;
 constexpr int kRowCapSmall = 64;
 constexpr int kRowCapLarge = 192;
 
@@ -117,11 +116,15 @@ template <class DT, int CAP, class KT>
 struct RowShared {
     static constexpr int TW = RowTile<DT>::TW;
     static constexpr int STRIDE = CAP + KT::kPad;  // keys per column row
-    alignas(16) typename KT::T cand[TW][STRIDE];   // per-column candidate keys
+    // The first pass's group maxima are read before any candidate is
+    // appended (a barrier lies between), so they share the candidates' space.
+    union {
+        alignas(16) typename KT::T cand[TW][STRIDE];  // per-column candidate keys
+        uint32_t reps[TW][kRowReps + 1];              // first-pass group maxima (orders)
+    };
     alignas(16) uint64_t tmp[kWaves][kMaxK];     // exact-path output per wave
     alignas(16) u32x4 qdata[kWaves][kRowQueue];  // queued row vectors
     uint32_t qmeta[kWaves][kRowQueue];           // (row << 3) | lane group of each queued vector
-    uint32_t reps[TW][kRowReps + 1];             // first-pass group maxima (orders)
     alignas(16) typename DT::storage fm[TW];     // raw-filter xor mask per column
     alignas(16) typename DT::storage fq[TW];     // raw-filter bound per column
     uint32_t thr[TW];                            // running threshold per column (order)
@@ -129,6 +132,12 @@ struct RowShared {
     uint32_t flag[TW];                           // 1: candidates overflowed, 2: negative NaN seen
     uint32_t ovf;                                // some column overflowed in this pass
 };
+
+static_assert(sizeof(uint32_t[RowTile<Bf16>::TW][kRowReps + 1]) <=
+                  sizeof(RowKey32::T[RowTile<Bf16>::TW][kRowCapSmall + RowKey32::kPad]) &&
+              sizeof(uint32_t[RowTile<F32>::TW][kRowReps + 1]) <=
+                  sizeof(RowKey64::T[RowTile<F32>::TW][kRowCapSmall + RowKey64::kPad]),
+              "the group maxima fit in the candidate area");
 
 __device__ __forceinline__ s16x2 as_s16x2_r(uint32_t w) { return __builtin_bit_cast(s16x2, w); }
 __device__ __forceinline__ u16x2 as_u16x2_r(uint32_t w) { return __builtin_bit_cast(u16x2, w); }
@@ -487,6 +496,11 @@ __device__ __noinline__ void rebuild_column(RowShared<DT, CAP, KT>& sh, const ty
         }
     }
 }
+
+// Three workgroups per CU when the candidate area allows (k <= kRowSmallK:
+// 47 KB of LDS); the register budget is then 168 per lane.
+template <class DT, int NV, int CAP, class KT>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void topk_row_scan(RowArgs a);
 
 template <class DT, int NV, int CAP, class KT>
 __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
