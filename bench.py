@@ -494,6 +494,71 @@ def trace_record(digest, w, config_n):
             for name, k in rec["kernels"].items()}
 
 
+SQ_PASSES = ("SQ_WAVES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VALU "
+             "SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VMEM",
+             "SQ_INSTS_VALU SQ_INSTS_LDS SQ_INSTS_SALU SQ_INSTS_VMEM_RD SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_LDS "
+             "SQ_INSTS_BRANCH SQ_ACTIVE_INST_SCA")
+
+
+def summarize_sq(dirs, config_n):
+    """Median per dispatch of the SQ counters of the top-k kernels over the
+    counter_collection.csv files of one or more 'rocprofv3 --pmc' runs of
+    '--profile N' (at most 8 SQ counters per run): written as
+    profiles/topk_*_cfgN_sq_counters.md with per-wave figures."""
+    from drafter_vocab_top_amd import workloads as W
+    w = W.config(config_n)
+    kinds = {}
+    for d in dirs:
+        import csv
+        for root, _, files in os.walk(d):
+            for fn in files:
+                if not fn.endswith("counter_collection.csv"):
+                    continue
+                with open(os.path.join(root, fn), newline="") as f:
+                    for rec in csv.DictReader(f):
+                        m = re.search(r"topk_\w+(<[^()]*>)?", rec.get("Kernel_Name", ""))
+                        if not m:
+                            continue
+                        key = (m.group(0), rec["Counter_Name"])
+                        per = kinds.setdefault(key, {})
+                        disp = int(rec.get("Dispatch_Id", "0"))
+                        per[disp] = per.get(disp, 0.0) + float(rec["Counter_Value"])
+    if not kinds:
+        raise SystemExit("no top-k counter records")
+    kernels = sorted({k for k, _ in kinds})
+    counters = sorted({c for _, c in kinds})
+    kind = "col" if w.layout == "col" else "row"
+    path = os.path.join(ROOT, "profiles", f"topk_{kind}_cfg{config_n}_sq_counters.md")
+    lines = [f"# SQ counters: {w.name}", "",
+             "Commands (from the repository root, on one MI355X; `cd /tmp && export TMPDIR=/tmp` first; "
+             "one run per line, at most 8 SQ counters each):", ""]
+    for i, names in enumerate(SQ_PASSES):
+        lines.append(f"    timeout -s KILL 60 rocprofv3 --pmc {names} -f csv -d {dirs[min(i, len(dirs) - 1)]} -o run "
+                     f"-- python3 bench.py --profile {config_n} --steps 10 --warmup 2")
+    lines.append(f"    python3 bench.py --summarize-sq {config_n} {' '.join(dirs)}")
+    lines += ["", f"Sources digest: `{kernel_sources_digest(w.layout)}`.  Medians over the dispatches of each kernel, "
+              "whole chip.  INSTS are instructions; ACTIVE, WAIT and BUSY are in the counters' own cycle units.", ""]
+    hdr = "| counter | " + " | ".join(f"`{k}` | per wave" for k in kernels) + " |"
+    lines += [hdr, "|---|" + "---|---|" * len(kernels)]
+    for c in counters:
+        row = f"| {c} |"
+        for k in kernels:
+            vals = sorted(kinds.get((k, c), {}).values())
+            waves = sorted(kinds.get((k, "SQ_WAVES"), {}).values())
+            if not vals:
+                row += " | |"
+                continue
+            med = vals[len(vals) // 2]
+            wv = waves[len(waves) // 2] if waves else 0
+            per_wave = f"{med / wv:,.0f}" if wv and c.startswith("SQ_INSTS") else ""
+            row += f" {med:,.0f} | {per_wave} |"
+        lines.append(row)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return path
+
+
 def traffic_record(digest, w, config_n):
     path = traffic_path(w, config_n)
     if not os.path.exists(path):
@@ -526,7 +591,14 @@ def main():
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "N"),
                     help="turn the kernel_trace.csv of a 'rocprofv3 --kernel-trace' run of '--profile N' "
                          "into profiles/topk_*_kernel_cfgN_ktrace.{json,md}")
+    ap.add_argument("--summarize-sq", nargs="+", metavar="N DIR",
+                    help="turn the counter_collection.csv files of SQ counter runs of '--profile N' "
+                         "into profiles/topk_*_cfgN_sq_counters.md")
     args = ap.parse_args()
+
+    if args.summarize_sq:
+        summarize_sq(args.summarize_sq[1:], int(args.summarize_sq[0]))
+        return
 
     if args.summarize_trace:
         summarize_trace(args.summarize_trace[0], int(args.summarize_trace[1]))

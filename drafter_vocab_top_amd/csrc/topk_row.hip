@@ -55,8 +55,9 @@
 //
 // Merge kernel: one wave per column selects the top k of its S sorted
 // partial lists (read with coalesced loads; the k-th largest of the S list
-// heads is the threshold, then a rank count) and writes the output.  The
-// kernel boundary orders it after the scan.
+// heads is the threshold, then a rank count, by 16-byte LDS broadcasts when
+// at most 64 keys pass) and writes the output.  The kernel boundary orders it
+// after the scan.
 #include <type_traits>
 
 #include "topk_device.hpp"
@@ -946,8 +947,8 @@ __global__ __launch_bounds__(kBlock) void topk_row_merge(RowArgs a) {
         const uint32_t idx = (uint32_t)j * 64u + lane;
         keys[j] = idx < M ? src[idx] : 0ull;
     }
-    // the threshold: k-th largest of the segment maxima (the head of each
-    // sorted list, lane l takes segments l, l + 64, ...)
+    // The threshold: the k-th largest of the segment maxima, the heads of
+    // the sorted lists (entry s*k of list s), one or a few lists per lane.
     uint64_t rep = 0;
     for (uint32_t sg = lane; sg < S; sg += 64u) rep = max_u64(rep, src[sg * k]);
     const uint32_t T = wave_kth_largest<OB>(key_order(rep), k);
@@ -955,22 +956,32 @@ __global__ __launch_bounds__(kBlock) void topk_row_merge(RowArgs a) {
 #pragma unroll
         for (int j = 0; j < KPL; ++j) f(keys[j], key_order(keys[j]) != 0);
     };
+    const storage* x = static_cast<const storage*>(a.x);
+    auto write_out = [&](uint32_t pos, uint64_t key) {
+        const uint32_t row = key_row(key), o = key_order(key);
+        static_cast<storage*>(a.out_values)[(int64_t)col * k + pos] =
+            (storage)((o == DT::kZeroOrder || o == DT::kNanOrder) ? (uint32_t)x[(int64_t)row * a.ld + col]
+                                                                  : DT::bits_from_order(o));
+        a.out_ids[(int64_t)col * k + pos] = a.id_map ? a.id_map[row] : (int32_t)row;
+    };
     uint32_t cnt = 0;
     visit([&](uint64_t key, bool valid) { cnt = wave_append(buf[wave], cnt, kBuf, valid && key_order(key) >= T, key); });
+    if (cnt <= 64u) {
+        // one candidate per lane: its rank decides its output slot
+        const uint32_t n8 = (cnt + 7u) & ~7u;
+        uint64_t key = 0;
+        if (lane < cnt) key = buf[wave][lane];
+        else if (lane < n8) buf[wave][lane] = 0;  // padding for the rank
+        const uint32_t r = lds_rank_of(buf[wave], n8, key);
+        if (lane < cnt && r < k) write_out(r, key);
+        return;
+    }
     uint32_t n;
     if (cnt > (uint32_t)kBuf)
         n = wave_exact_topk<OB>(buf[wave], kBuf, tmp[wave], visit, k);
     else
         n = wave_rank_select(buf[wave], cnt, k, tmp[wave]);
-    if (lane < k && lane < n) {
-        const uint64_t key = tmp[wave][lane];
-        const uint32_t row = key_row(key), o = key_order(key);
-        const storage* x = static_cast<const storage*>(a.x);
-        static_cast<storage*>(a.out_values)[(int64_t)col * k + lane] =
-            (storage)((o == DT::kZeroOrder || o == DT::kNanOrder) ? (uint32_t)x[(int64_t)row * a.ld + col]
-                                                                  : DT::bits_from_order(o));
-        a.out_ids[(int64_t)col * k + lane] = a.id_map ? a.id_map[row] : (int32_t)row;
-    }
+    if (lane < k && lane < n) write_out(lane, tmp[wave][lane]);
 }
 
 template <class DT, int CAP, class KT>
