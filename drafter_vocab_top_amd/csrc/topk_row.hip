@@ -53,11 +53,11 @@
 // a column, like one that still overflows after a rebuild (massive ties), is
 // re-read over the whole segment by one wave and selected by an exact search.
 //
-// Merge kernel: one wave per column selects the top k of its S sorted
-// partial lists (read with coalesced loads; the k-th largest of the S list
-// heads is the threshold, then a rank count, by 16-byte LDS broadcasts when
-// at most 64 keys pass) and writes the output.  The kernel boundary orders it
-// after the scan.
+// Merge kernel: one workgroup per column selects the top k of its S sorted
+// partial lists (its four waves read a quarter of the entries each with
+// coalesced loads; the k-th largest of the S list heads is the threshold,
+// then a rank count, by 16-byte LDS broadcasts when at most 64 entries pass)
+// and writes the output.  The kernel boundary orders it after the scan.
 #include <type_traits>
 
 #include "topk_device.hpp"
@@ -924,38 +924,56 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
     }
 }
 
-// One wave per column: the top k of the column's S partial lists.
+// One workgroup per column: the top k of the column's S partial lists.  The
+// four waves split the column's S*k list entries (coalesced: load j of wave
+// w gives lane l entry (w*KW + j)*64 + l).  Each wave takes the same
+// threshold, the k-th largest of the S list heads (each list is sorted, so k
+// distinct entries reach it), and appends its entries at or above it to the
+// workgroup's buffer behind the other waves' (one LDS atomic per wave).
+// Wave 0 ranks them and writes the output.  A column whose candidates
+// overflow the buffer (massive ties) is merged by wave 0 with the exact
+// search over all entries, re-read from memory at each step.
 template <class DT, int KPL>
 __global__ __launch_bounds__(kBlock) void topk_row_merge(RowArgs a) {
     using storage = typename DT::storage;
     constexpr int OB = DT::kOrderBits;
+    constexpr int KW = KPL / kWaves;  // loads per lane in each wave
+    static_assert(KPL % kWaves == 0, "whole loads per wave");
     constexpr int kBuf = kMaxK + 192;
-    __shared__ alignas(16) uint64_t buf[kWaves][kBuf];
-    __shared__ alignas(16) uint64_t tmp[kWaves][kMaxK];
+    __shared__ alignas(16) uint64_t cand[kBuf];
+    __shared__ alignas(16) uint64_t best[kMaxK];
+    __shared__ uint32_t ncand;
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
-    const uint32_t col = blockIdx.x * kWaves + wave;
-    if (col >= (uint32_t)a.C) return;
+    const uint32_t col = blockIdx.x;
     const uint32_t k = (uint32_t)a.k, S = (uint32_t)a.S, M = S * k;
     const uint64_t* src = a.partials + (int64_t)col * M;
+    if (threadIdx.x == 0) ncand = 0;
     // the scan is over: clear the column's shared-bound slots for the next run
-    if (a.use_bound && lane < (uint32_t)kRowBoundSlots) a.bound[(int64_t)col * kRowBoundSlots + lane] = 0u;
-    // Coalesced loads: load j gives lane l entry j*64 + l of the column's S
-    // lists.
-    uint64_t keys[KPL];
+    if (wave == 0 && a.use_bound && lane < (uint32_t)kRowBoundSlots)
+        a.bound[(int64_t)col * kRowBoundSlots + lane] = 0u;
+    uint64_t keys[KW];
 #pragma unroll
-    for (int j = 0; j < KPL; ++j) {
-        const uint32_t idx = (uint32_t)j * 64u + lane;
+    for (int j = 0; j < KW; ++j) {
+        const uint32_t idx = (wave * (uint32_t)KW + (uint32_t)j) * 64u + lane;
         keys[j] = idx < M ? src[idx] : 0ull;
     }
-    // The threshold: the k-th largest of the segment maxima, the heads of
-    // the sorted lists (entry s*k of list s), one or a few lists per lane.
     uint64_t rep = 0;
     for (uint32_t sg = lane; sg < S; sg += 64u) rep = max_u64(rep, src[sg * k]);
     const uint32_t T = wave_kth_largest<OB>(key_order(rep), k);
-    auto visit = [&](auto&& f) {
+    // sentinel entries (order 0, from segments with fewer than k rows) never qualify
+    auto passes = [&](uint64_t key) { return key_order(key) != 0u && key_order(key) >= T; };
+    uint32_t mine = 0;
 #pragma unroll
-        for (int j = 0; j < KPL; ++j) f(keys[j], key_order(keys[j]) != 0);
-    };
+    for (int j = 0; j < KW; ++j) mine += (uint32_t)__popcll(__ballot(passes(keys[j])));
+    __syncthreads();  // ncand is zero
+    uint32_t base = 0;
+    if (lane == 0 && mine != 0u) base = atomicAdd(&ncand, mine);
+    uint32_t cnt = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+#pragma unroll
+    for (int j = 0; j < KW; ++j) cnt = wave_append(cand, cnt, (uint32_t)kBuf, passes(keys[j]), keys[j]);
+    __syncthreads();
+    if (wave != 0) return;
+
     const storage* x = static_cast<const storage*>(a.x);
     auto write_out = [&](uint32_t pos, uint64_t key) {
         const uint32_t row = key_row(key), o = key_order(key);
@@ -964,24 +982,31 @@ __global__ __launch_bounds__(kBlock) void topk_row_merge(RowArgs a) {
                                                                   : DT::bits_from_order(o));
         a.out_ids[(int64_t)col * k + pos] = a.id_map ? a.id_map[row] : (int32_t)row;
     };
-    uint32_t cnt = 0;
-    visit([&](uint64_t key, bool valid) { cnt = wave_append(buf[wave], cnt, kBuf, valid && key_order(key) >= T, key); });
-    if (cnt <= 64u) {
+    const uint32_t n = ncand;
+    if (n <= 64u) {
         // one candidate per lane: its rank decides its output slot
-        const uint32_t n8 = (cnt + 7u) & ~7u;
+        const uint32_t n8 = (n + 7u) & ~7u;
         uint64_t key = 0;
-        if (lane < cnt) key = buf[wave][lane];
-        else if (lane < n8) buf[wave][lane] = 0;  // padding for the rank
-        const uint32_t r = lds_rank_of(buf[wave], n8, key);
-        if (lane < cnt && r < k) write_out(r, key);
+        if (lane < n) key = cand[lane];
+        else if (lane < n8) cand[lane] = 0;  // padding for the rank
+        const uint32_t r = lds_rank_of(cand, n8, key);
+        if (lane < n && r < k) write_out(r, key);
         return;
     }
-    uint32_t n;
-    if (cnt > (uint32_t)kBuf)
-        n = wave_exact_topk<OB>(buf[wave], kBuf, tmp[wave], visit, k);
-    else
-        n = wave_rank_select(buf[wave], cnt, k, tmp[wave]);
-    if (lane < k && lane < n) write_out(lane, tmp[wave][lane]);
+    uint32_t m;
+    if (n <= (uint32_t)kBuf) {
+        m = wave_rank_select(cand, n, k, best);
+    } else {
+        auto visit = [&](auto&& f) {
+#pragma unroll 1
+            for (uint32_t i = lane; i < KPL * 64u; i += 64u) {
+                const uint64_t key = i < M ? src[i] : 0ull;
+                f(key, key_order(key) != 0u);
+            }
+        };
+        m = wave_exact_topk<OB>(cand, (uint32_t)kBuf, best, visit, k);
+    }
+    if (lane < k && lane < m) write_out(lane, best[lane]);
 }
 
 template <class DT, int CAP, class KT>
@@ -1011,7 +1036,7 @@ hipError_t launch_row_dt(int nv, const RowArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     // keys per lane: S*k entries over 64 lanes, in the smallest register
     // bucket that holds them (every slot is visited in the selection)
-    const dim3 mgrid((uint32_t)((a.C + kWaves - 1) / kWaves));
+    const dim3 mgrid((uint32_t)a.C);
     const int64_t m = (int64_t)a.S * a.k;
     if (m <= 16 * 64)
         hipLaunchKernelGGL((topk_row_merge<DT, 16>), mgrid, dim3(kBlock), 0, stream, a);
