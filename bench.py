@@ -559,6 +559,53 @@ def summarize_sq(dirs, config_n):
     return path
 
 
+READREQ_COUNTERS = "TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum TCC_EA0_RDREQ_128B_sum"
+
+
+def summarize_readreq(directory, config_n):
+    """Read requests from L2 to memory by size, per dispatch (medians), for
+    the top-k kernels and the calibration copy of a '--profile N' run:
+    bytes = 32 n32 + 64 n64 + 128 n128, with no scaling.  Written as
+    profiles/topk_*_cfgN_read_requests.md."""
+    from drafter_vocab_top_amd import workloads as W
+    w = W.config(config_n)
+    names = READREQ_COUNTERS.split()
+    per = {}
+    for name in names:
+        rows = _counter_rows(directory, name)
+        copies = sorted((disp, v) for (kn, disp), v in rows.items() if "copyBuffer" in kn)[-5:]
+        per.setdefault("copy", {})[name] = statistics.median(v for _, v in copies) if copies else float("nan")
+        for (kn, _), v in rows.items():
+            m = re.search(r"topk_\w+(<[^()]*>)?", kn)
+            if m:
+                per.setdefault(m.group(0), {}).setdefault(name, []).append(v)
+    out = {}
+    for kn, d in per.items():
+        med = {c: (statistics.median(v) if isinstance(v, list) else v) for c, v in d.items()}
+        n32, n64, n128 = med["TCC_EA0_RDREQ_32B_sum"], med["TCC_EA0_RDREQ_64B_sum"], med["TCC_EA0_RDREQ_128B_sum"]
+        out[kn] = dict(med, bytes=32 * n32 + 64 * n64 + 128 * n128)
+    kind = "col" if w.layout == "col" else "row"
+    path = os.path.join(ROOT, "profiles", f"topk_{kind}_cfg{config_n}_read_requests.md")
+    lines = [f"# Read requests from L2 to memory, by size: {w.name}", "",
+             "Command (from the repository root, on one MI355X; `cd /tmp && export TMPDIR=/tmp` first):", "",
+             f"    timeout -s KILL 60 rocprofv3 --pmc {READREQ_COUNTERS} -f csv -d {directory} -o run "
+             f"-- python3 bench.py --profile {config_n} --steps 10 --warmup 2",
+             f"    python3 bench.py --summarize-readreq {directory} {config_n}", "",
+             f"Sources digest: `{kernel_sources_digest(w.layout)}`.  Medians per dispatch.  `copy` is the plain "
+             f"copy of {COPY_BYTES:,} bytes that ends the run.  Bytes = 32 n32 + 64 n64 + 128 n128.", "",
+             "| kernel | requests | 32 B | 64 B | 128 B | bytes read | algorithmic bytes |",
+             "|---|---|---|---|---|---|---|"]
+    for kn, d in out.items():
+        alg = COPY_BYTES if kn == "copy" else algorithmic_bytes(w)
+        lines.append(f"| `{kn}` | {d['TCC_EA0_RDREQ_sum']:,.0f} | {d['TCC_EA0_RDREQ_32B_sum']:,.0f} | "
+                     f"{d['TCC_EA0_RDREQ_64B_sum']:,.0f} | {d['TCC_EA0_RDREQ_128B_sum']:,.0f} | {d['bytes']:,.0f} | "
+                     f"{alg:,} |")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return out
+
+
 def traffic_record(digest, w, config_n):
     path = traffic_path(w, config_n)
     if not os.path.exists(path):
@@ -594,7 +641,14 @@ def main():
     ap.add_argument("--summarize-sq", nargs="+", metavar="N DIR",
                     help="turn the counter_collection.csv files of SQ counter runs of '--profile N' "
                          "into profiles/topk_*_cfgN_sq_counters.md")
+    ap.add_argument("--summarize-readreq", nargs=2, metavar=("DIR", "N"),
+                    help="turn a read-request-size counter run of '--profile N' into "
+                         "profiles/topk_*_cfgN_read_requests.md")
     args = ap.parse_args()
+
+    if args.summarize_readreq:
+        summarize_readreq(args.summarize_readreq[0], int(args.summarize_readreq[1]))
+        return
 
     if args.summarize_sq:
         summarize_sq(args.summarize_sq[1:], int(args.summarize_sq[0]))
