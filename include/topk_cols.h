@@ -232,7 +232,7 @@ const char *topk_cols_status_string(int status);
  *
  * Returns the errors of topk_cols_create for a bad shape, and
  * TOPK_ERR_UNSUPPORTED when C > 4096 or the shape's workspace exceeds the
- * array (for example 248,046 x 448 bf16 rows with k = 16 needs 4.2 MiB and
+ * array (for example 248,046 x 448 bf16 rows with k = 16 needs 7.0 MiB and
  * fits); TOPK_ERR_INVALID_ARG for a NULL or misaligned pointer;
  * TOPK_ERR_HIP when there is no device or the launch fails.
  */
