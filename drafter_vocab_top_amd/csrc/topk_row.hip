@@ -499,7 +499,9 @@ __device__ __noinline__ void rebuild_column(RowShared<DT, CAP, KT>& sh, const ty
 }
 
 // Three workgroups per CU when the candidate area allows (k <= kRowSmallK:
-// 47 KB of LDS); the register budget is then 168 per lane.
+// 47 KB of LDS); the register budget is then 168 per lane.  The larger
+// candidate areas allow fewer workgroups whatever the registers, and the
+// compiler says so (the build silences that note for this file).
 template <class DT, int NV, int CAP, class KT>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void topk_row_scan(RowArgs a);
 
