@@ -97,6 +97,13 @@ class Rotation:
         torch.cuda.synchronize()
 
 
+def rotation_order(R, warmup, steps, per_call):
+    """Copy indices of the warm-up, timed and per-call calls: one sequence
+    over the R copies, so a copy is read again only after all R have been."""
+    seq = [i % R for i in range(warmup + steps + per_call)]
+    return seq[:warmup], seq[warmup:warmup + steps], seq[warmup + steps:]
+
+
 def time_config(torch, T, w, steps, warmup, per_call_steps=None, warm=True, algo="auto"):
     """Amortized and per-call timings of one workload (cold HBM by rotation)."""
     import numpy as np
@@ -114,29 +121,29 @@ def time_config(torch, T, w, steps, warmup, per_call_steps=None, warm=True, algo
     # the copies are read in one sequence: warm-up, timed region, per-call
     # region; a copy is read again only after all R copies (>= 1 GiB) have
     # been read since, so no timed call finds its input in a cache
-    for s in range(warmup):
-        run(hh, ptrs[s % R], pv, pi, sp)
+    n_pc = per_call_steps or steps
+    warm_idx, timed_idx, pc_idx = rotation_order(R, warmup, steps, n_pc)
+    for i in warm_idx:
+        run(hh, ptrs[i], pv, pi, sp)
     torch.cuda.synchronize()
 
     # amortized: one event pair around `steps` back-to-back calls
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_host = time.perf_counter()
     e0.record(stream)
-    for s in range(warmup, warmup + steps):
-        run(hh, ptrs[s % R], pv, pi, sp)
+    for i in timed_idx:
+        run(hh, ptrs[i], pv, pi, sp)
     e1.record(stream)
     host_us = (time.perf_counter() - t_host) * 1e6 / steps
     e1.synchronize()
     amort_us = e0.elapsed_time(e1) * 1000.0 / steps
 
     # per call: an event pair around each call, all enqueued back to back
-    n_pc = per_call_steps or steps
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_pc)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_pc)]
-    first = warmup + steps
-    for s in range(n_pc):
+    for s, i in enumerate(pc_idx):
         starts[s].record(stream)
-        run(hh, ptrs[(first + s) % R], pv, pi, sp)
+        run(hh, ptrs[i], pv, pi, sp)
         ends[s].record(stream)
     torch.cuda.synchronize()
     per_call = sorted(starts[s].elapsed_time(ends[s]) * 1000.0 for s in range(n_pc))
@@ -165,7 +172,7 @@ def time_config(torch, T, w, steps, warmup, per_call_steps=None, warm=True, algo
         res["warm_us_per_round"] = e0.elapsed_time(e1) * 1000.0 / steps
     # the timed outputs must be the right answer: compare the last call's
     # result with a fresh run on the same input (cheap self-check)
-    run(hh, ptrs[(first + n_pc - 1) % R], pv, pi, sp)
+    run(hh, ptrs[pc_idx[-1]], pv, pi, sp)
     torch.cuda.synchronize()
     res["_last"] = (vals.cpu().numpy(), ids.cpu().numpy())
     h.close()
@@ -500,7 +507,7 @@ SQ_PASSES = ("SQ_WAVES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INS
              "SQ_INSTS_BRANCH SQ_ACTIVE_INST_SCA")
 
 
-def summarize_sq(dirs, config_n):
+def summarize_sq(dirs, config_n, out_path=None):
     """Median per dispatch of the SQ counters of the top-k kernels over the
     counter_collection.csv files of one or more 'rocprofv3 --pmc' runs of
     '--profile N' (at most 8 SQ counters per run): written as
@@ -528,7 +535,7 @@ def summarize_sq(dirs, config_n):
     kernels = sorted({k for k, _ in kinds})
     counters = sorted({c for _, c in kinds})
     kind = "col" if w.layout == "col" else "row"
-    path = os.path.join(ROOT, "profiles", f"topk_{kind}_cfg{config_n}_sq_counters.md")
+    path = out_path or os.path.join(ROOT, "profiles", f"topk_{kind}_cfg{config_n}_sq_counters.md")
     lines = [f"# SQ counters: {w.name}", "",
              "Commands (from the repository root, on one MI355X; `cd /tmp && export TMPDIR=/tmp` first; "
              "one run per line, at most 8 SQ counters each):", ""]
@@ -562,7 +569,7 @@ def summarize_sq(dirs, config_n):
 READREQ_COUNTERS = "TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum TCC_EA0_RDREQ_128B_sum"
 
 
-def summarize_readreq(directory, config_n):
+def summarize_readreq(directory, config_n, out_path=None):
     """Read requests from L2 to memory by size, per dispatch (medians), for
     the top-k kernels and the calibration copy of a '--profile N' run:
     bytes = 32 n32 + 64 n64 + 128 n128, with no scaling.  Written as
@@ -585,7 +592,7 @@ def summarize_readreq(directory, config_n):
         n32, n64, n128 = med["TCC_EA0_RDREQ_32B_sum"], med["TCC_EA0_RDREQ_64B_sum"], med["TCC_EA0_RDREQ_128B_sum"]
         out[kn] = dict(med, bytes=32 * n32 + 64 * n64 + 128 * n128)
     kind = "col" if w.layout == "col" else "row"
-    path = os.path.join(ROOT, "profiles", f"topk_{kind}_cfg{config_n}_read_requests.md")
+    path = out_path or os.path.join(ROOT, "profiles", f"topk_{kind}_cfg{config_n}_read_requests.md")
     lines = [f"# Read requests from L2 to memory, by size: {w.name}", "",
              "Command (from the repository root, on one MI355X; `cd /tmp && export TMPDIR=/tmp` first):", "",
              f"    timeout -s KILL 60 rocprofv3 --pmc {READREQ_COUNTERS} -f csv -d {directory} -o run "
