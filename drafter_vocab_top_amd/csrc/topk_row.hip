@@ -959,8 +959,12 @@ __global__ __launch_bounds__(kBlock) void topk_row_merge(RowArgs a) {
         const uint32_t idx = (wave * (uint32_t)KW + (uint32_t)j) * 64u + lane;
         keys[j] = idx < M ? src[idx] : 0ull;
     }
-    uint64_t rep = 0;
-    for (uint32_t sg = lane; sg < S; sg += 64u) rep = max_u64(rep, src[sg * k]);
+    // the list heads, two per lane issued together (S <= 128 whenever
+    // k >= 16), more in a loop
+    const uint64_t h0 = lane < S ? src[lane * k] : 0ull;
+    const uint64_t h1 = lane + 64u < S ? src[(lane + 64u) * k] : 0ull;
+    uint64_t rep = max_u64(h0, h1);
+    for (uint32_t sg = lane + 128u; sg < S; sg += 64u) rep = max_u64(rep, src[sg * k]);
     const uint32_t T = wave_kth_largest<OB>(key_order(rep), k);
     // sentinel entries (order 0, from segments with fewer than k rows) never qualify
     auto passes = [&](uint64_t key) { return key_order(key) != 0u && key_order(key) >= T; };
