@@ -181,3 +181,22 @@ def test_overflow_rebuild_with_shared_bound(gpu, kind, dtype, V, segments):
     print(f"[parity-row] overflow and rebuild, {kind} {dtype} V={V} C={C} k={k} segments={segments}", flush=True)
     assert_parity(gpu, x, V, C, k, dtype, W.ROW, C, segments=segments,
                   label=f"row {kind} {dtype} V={V} segments={segments}")
+
+
+def test_merge_candidate_counts(gpu):
+    """The merge kernel's three selection paths, at the full row count (109
+    segments of 16-entry lists): a value above every other planted at N rows
+    of a column makes about N list entries reach the merge's threshold.
+    N = 30 ranks them in one wave (at most 64), N = 150 by the workgroup's
+    rank selection, N = 600 overflows the candidate buffer (the exact search
+    that re-reads the lists)."""
+    V, C, k = 248046, 64, 16
+    x = W.random_matrix(5150, V, C, W.BF16, W.ROW)
+    rng = np.random.default_rng(5151)
+    big = 0x4220  # bf16 40.0, above every N(0, 4^2) sample here
+    for c in range(C):
+        n = (30, 150, 600)[c % 3]
+        rows = rng.choice(V, size=n, replace=False)
+        x[rows, c] = big
+    print(f"[parity-row] merge candidate counts 30/150/600, V={V} C={C} k={k}", flush=True)
+    assert_parity(gpu, x, V, C, k, W.BF16, W.ROW, C, label="row merge candidate counts")
