@@ -105,6 +105,25 @@ def test_ties_and_monotone_columns(gpu, dtype, kind):
             assert_parity(gpu, x, V, C, k, dtype, W.COL, V, segments=seg, label=f"{kind} k={k} seg={seg}")
 
 
+@pytest.mark.parametrize("n_cols,k", [(7, 8), (56, 8), (56, 20)])
+def test_tied_top_counts(gpu, n_cols, k):
+    """The selection paths of a workgroup and of a column's merger at full
+    column length: a value above every other, planted at N rows of a column,
+    makes about N/S of each segment's elements and about N list entries tie
+    at the top.  N = 20 and 100 keep each segment's candidates within one
+    wave's LDS rank; N = 2,000 and 5,000 put 50-300 candidates in a segment
+    and every list entry of the column in the merger's rank selection."""
+    V = 248046
+    x = W.random_matrix(6160 + n_cols + k, V, n_cols, W.BF16, W.COL)
+    rng = np.random.default_rng(6161)
+    big = 0x4220  # bf16 40.0, above every N(0, 4^2) sample here
+    for c in range(n_cols):
+        n = (20, 100, 2000, 5000)[c % 4]
+        x[c, rng.choice(V, size=n, replace=False)] = big
+    print(f"[parity] tied top counts 20/100/2000/5000, V={V} C={n_cols} k={k}", flush=True)
+    assert_parity(gpu, x, V, n_cols, k, W.BF16, W.COL, V, label=f"tied top counts C={n_cols} k={k}")
+
+
 @pytest.mark.parametrize("dtype", [W.BF16, W.F32])
 def test_negative_and_nan_columns(gpu, dtype):
     """All-negative columns (log-probability-like), columns with negative NaNs,
