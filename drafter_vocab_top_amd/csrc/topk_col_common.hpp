@@ -85,70 +85,6 @@ __device__ __forceinline__ void lane_stats(const u32x4 (&d)[NV], uint32_t (&vmax
     }
 }
 
-// The cheaper lane statistics of one pass, for the common case:
-//   vmax[i]: raw signed maximum of vector i (bf16: two 16-bit halves packed)
-//   smax:    the lane's largest raw signed pattern; when it is >= 0 it is the
-//            lane's largest value, else lane_rep_negative gives that value
-//   neg_nan: the lane holds a negative NaN
-// Invalid vector slots hold -Inf patterns, which never raise a maximum.
-template <class DT, int NV>
-__device__ __forceinline__ void lane_max(const u32x4 (&d)[NV], uint32_t (&vmax)[NV], int& smax, bool& neg_nan) {
-    if constexpr (DT::kPerVec == 8) {
-        s16x2 sm = {-32768, -32768};
-        u16x2 um = {0, 0};
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const uint32_t wx = d[i].x, wy = d[i].y, wz = d[i].z, ww = d[i].w;
-            const s16x2 mx = __builtin_elementwise_max(__builtin_elementwise_max(as_s16x2(wx), as_s16x2(wy)),
-                                                       __builtin_elementwise_max(as_s16x2(wz), as_s16x2(ww)));
-            const u16x2 ux = __builtin_elementwise_max(__builtin_elementwise_max(as_u16x2(wx), as_u16x2(wy)),
-                                                       __builtin_elementwise_max(as_u16x2(wz), as_u16x2(ww)));
-            vmax[i] = __builtin_bit_cast(uint32_t, mx);
-            sm = __builtin_elementwise_max(sm, mx);
-            um = __builtin_elementwise_max(um, ux);
-        }
-        smax = max_i32((int)sm.x, (int)sm.y);
-        neg_nan = max_u32((uint32_t)um.x, (uint32_t)um.y) > 0xFF80u;
-    } else {
-        int sm = INT32_MIN;
-        uint32_t um = 0;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const uint32_t wx = d[i].x, wy = d[i].y, wz = d[i].z, ww = d[i].w;
-            const int mx = max_i32(max_i32((int)wx, (int)wy), max_i32((int)wz, (int)ww));
-            vmax[i] = (uint32_t)mx;
-            sm = max_i32(sm, mx);
-            um = max_u32(um, max_u32(max_u32(wx, wy), max_u32(wz, ww)));
-        }
-        smax = sm;
-        neg_nan = um > 0xFF800000u;
-    }
-}
-
-// The largest order of a lane whose patterns are all negative: the signed
-// minimum (the negative value nearest zero).
-template <class DT, int NV>
-__device__ __forceinline__ uint32_t lane_rep_negative(const u32x4 (&d)[NV]) {
-    if constexpr (DT::kPerVec == 8) {
-        s16x2 sn = {32767, 32767};
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const uint32_t wx = d[i].x, wy = d[i].y, wz = d[i].z, ww = d[i].w;
-            sn = __builtin_elementwise_min(sn, __builtin_elementwise_min(
-                __builtin_elementwise_min(as_s16x2(wx), as_s16x2(wy)), __builtin_elementwise_min(as_s16x2(wz), as_s16x2(ww))));
-        }
-        return order_bf16((uint32_t)min_i32((int)sn.x, (int)sn.y) & 0xFFFFu);
-    } else {
-        int sn = INT32_MAX;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const uint32_t wx = d[i].x, wy = d[i].y, wz = d[i].z, ww = d[i].w;
-            sn = min_i32(sn, min_i32(min_i32((int)wx, (int)wy), min_i32((int)wz, (int)ww)));
-        }
-        return order_f32((uint32_t)sn);
-    }
-}
-
 // Signed maximum held in a vmax entry.
 template <class DT>
 __device__ __forceinline__ int vec_max_signed(uint32_t vm) {
