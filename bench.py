@@ -14,25 +14,31 @@ Cache.
 The script prints one JSON line on stdout.  Progress goes to stderr.
   value / ms_per_step  microseconds (milliseconds) per round: K back-to-back
                        calls between two events on the launch stream, divided
-                       by K.
+                       by K.  The calls read the copies in one sequence after
+                       the warm-up's, so none finds its input in a cache.
   roofline             algorithmic bytes per launch (every element read once
-                       plus the outputs written), divided by the mean launch
-                       duration over the timed region (the same K calls and
-                       events as value).  Peak is 8 TB/s HBM3E.  traffic is the HBM bytes per launch measured by
-                       rocprofv3 counters, scaled by a plain copy of known
-                       size (profiles/*_traffic.json).  It is null when the
-                       kernel source changed after the counters were taken.
+                       plus the outputs written) divided by the per-launch
+                       event time of the same K calls (event_us_per_launch),
+                       against 8 TB/s HBM3E.  kernel_trace: the kernel-only
+                       mean and median from the committed rocprofv3 trace
+                       summary (profiles/*_ktrace.json); traffic: HBM bytes
+                       per launch from rocprofv3 counters, scaled by a plain
+                       copy of known size (profiles/*_traffic.json).  Both
+                       are null when the kernel sources changed since.
   per_config           the same measurements for all five workloads, with the
-                       launch floor of an empty kernel and the warm-cache
-                       figure; for the column-contiguous workloads also the
-                       one-wave-per-column baseline kernel (the design the
-                       page replaced) under the same protocol, and for all a
-                       plain streaming read of the same bytes
-                       (stream_read.hip) as the achievable-bandwidth
-                       reference, and the sampler that can follow the
-                       top-k (topk_cols_sample, T = 1, top_p = 0.95).
-  cpu_baseline         the CPU oracle timed on this host's cores on whole
-                       rounds of the headline workload.
+                       per-call median, the warm-cache figure and the
+                       per-call time of the same calls captured in one HIP
+                       graph and replayed; for the column-contiguous
+                       workloads also the one-wave-per-column baseline kernel
+                       (the design the page replaced); for all a plain
+                       streaming read of the same bytes (stream_read.hip) as
+                       the achievable-bandwidth reference, and the sampler
+                       that can follow the top-k (topk_cols_sample, T = 1,
+                       top_p = 0.95).
+  launch_floor_us      an empty kernel replayed from a graph;
+  launch_floor_eager_us  the same kernel launched by eager ctypes calls.
+  cpu_baseline         the CPU oracle on whole rounds of the headline workload
+                       on min(C, cores) threads, and on one thread.
 """
 from __future__ import annotations
 
@@ -104,7 +110,7 @@ def rotation_order(R, warmup, steps, per_call):
     return seq[:warmup], seq[warmup:warmup + steps], seq[warmup + steps:]
 
 
-def time_config(torch, T, w, steps, warmup, per_call_steps=None, warm=True, algo="auto"):
+def time_config(torch, T, w, steps, warmup, per_call_steps=None, warm=True, algo="auto", graph=False):
     """Amortized and per-call timings of one workload (cold HBM by rotation)."""
     import numpy as np
     rot = Rotation(torch, w)
@@ -170,6 +176,28 @@ def time_config(torch, T, w, steps, warmup, per_call_steps=None, warm=True, algo
         e1.record(stream)
         e1.synchronize()
         res["warm_us_per_round"] = e0.elapsed_time(e1) * 1000.0 / steps
+    if graph:
+        # the same calls captured in one HIP graph (one call per copy, in
+        # rotation order) and replayed back to back: what a caller that
+        # captures its decode step sees per call
+        gs = torch.cuda.Stream()
+        with torch.cuda.stream(gs):
+            run(hh, ptrs[0], pv, pi, gs.cuda_stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gs):
+            for i in range(R):
+                run(hh, ptrs[i], pv, pi, gs.cuda_stream)
+        reps = max(2, -(-steps // R))
+        with torch.cuda.stream(gs):
+            g.replay()
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+        e1.synchronize()
+        res["graph_us_per_call"] = e0.elapsed_time(e1) * 1000.0 / (reps * R)
+        del g
     # the timed outputs must be the right answer: compare the last call's
     # result with a fresh run on the same input (cheap self-check)
     run(hh, ptrs[pc_idx[-1]], pv, pi, sp)
@@ -713,7 +741,7 @@ def main():
         warmup = args.warmup if n == HEADLINE else 50
         log(f"timing {w.name}: {steps} steps, warmup {warmup}")
         try:
-            r = time_config(torch, T, w, steps, warmup)
+            r = time_config(torch, T, w, steps, warmup, graph=True)
         except T.TopkError as e:
             per_config[f"cfg{n}"] = {"workload": w.name, "error": str(e)}
             log(f"  {e}")
@@ -740,6 +768,7 @@ def main():
         })
         per_config[f"cfg{n}"] = r
         log(f"  {r['us_per_round']:.2f} us/round (per call {r['per_call_median_us']:.2f} us, "
+            f"graph replay {r.get('graph_us_per_call', float('nan')):.2f} us, "
             f"warm {r.get('warm_us_per_round', float('nan')):.2f} us, host {r['host_enqueue_us_per_call']:.2f} us), "
             f"{r['gbps']:.0f} GB/s = {100 * r['frac_of_peak']:.1f}% of peak, exact={exact}")
         try:
