@@ -92,7 +92,7 @@ int make_plan(Plan* plan, int64_t V, int64_t C, int32_t k, int32_t dtype, int32_
     if (row && algo != TOPK_ALGO_AUTO) return TOPK_ERR_UNSUPPORTED;
     if (row && forced_segments * k > kRowMaxMergeKeys) return TOPK_ERR_UNSUPPORTED;
     if (algo == TOPK_ALGO_ONE_WAVE && forced_segments > 1) return TOPK_ERR_UNSUPPORTED;  // no split
-    if (C > 0x7FFFFFFF) return TOPK_ERR_UNSUPPORTED;
+    if (C > 0x7FFFFFFF || (row && row_bound_ld(C) > 0x7FFFFFFF)) return TOPK_ERR_UNSUPPORTED;
     if (cu_count < 1) return TOPK_ERR_HIP;
 
     if (!row && algo == TOPK_ALGO_AUTO) algo = TOPK_ALGO_WORKGROUP;
@@ -117,7 +117,8 @@ int make_plan(Plan* plan, int64_t V, int64_t C, int32_t k, int32_t dtype, int32_
     // one list of k keys per segment and column
     const size_t list_bytes = align256((size_t)C * (size_t)S * (size_t)k * sizeof(uint64_t));
     p.bound_off = p.list_off + list_bytes;
-    const size_t bound_bytes = row ? align256((size_t)C * kRowBoundSlots * sizeof(uint32_t)) : 0;
+    const size_t bound_bytes =
+        row ? align256((size_t)row_bound_ld(C) * kRowBoundRows * sizeof(uint32_t)) : 0;
     p.workspace_bytes = p.bound_off + bound_bytes;
     *plan = p;
     return TOPK_OK;
@@ -142,7 +143,8 @@ hipError_t launch_plan(const Plan& h, void* ws, int64_t n_cols, const void* logi
         a.key32 = (h.dtype == TOPK_BF16 && ceil_div(h.V, h.segments) <= 65536) ? 1 : 0;
         a.partials = partials;
         a.bound = reinterpret_cast<uint32_t*>(base + h.bound_off);
-        a.use_bound = h.k <= kRowBoundSlots ? 1 : 0;
+        a.bound_ld = (int32_t)row_bound_ld(h.C);
+        a.use_bound = h.k <= kRowBoundMaxK && h.segments >= h.k ? 1 : 0;
         a.out_values = out_values;
         a.out_ids = out_ids;
         a.id_map = id_map;

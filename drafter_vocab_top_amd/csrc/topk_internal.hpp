@@ -62,8 +62,9 @@ struct RowArgs {
     int32_t vec_loads;    // 1 if every row start of a tile is 16-byte aligned
     int32_t key32;        // 1: bf16 and segments of at most 65,536 rows (32-bit candidate keys)
     uint64_t* partials;   // C*S*k keys
-    uint32_t* bound;      // C*kRowBoundSlots orders, zero between runs (see the row scan)
-    int32_t use_bound;    // 1 if k <= kRowBoundSlots: segments share a lower bound per column
+    uint32_t* bound;      // kRowBoundRows rows of bound_ld orders, zero between runs (see the row scan)
+    int32_t bound_ld;     // words per bound row: at least C, a multiple of 64
+    int32_t use_bound;    // 1 if k <= kRowBoundMaxK and S >= k: segments share a lower bound per column
     void* out_values;     // C*k elements of the input dtype
     int32_t* out_ids;     // C*k
     const int32_t* id_map;  // NULL, or V entries: out_ids holds id_map[row] instead of row
@@ -73,7 +74,14 @@ constexpr int kRowMaxMergeKeys = 2048;
 // Row scans with k <= kRowSmallK keep a smaller candidate area and run three
 // workgroups per CU; larger k, two.
 constexpr int kRowSmallK = 16;
-constexpr int kRowBoundSlots = 16;
+// Row segments below kRowBoundRows store one element per column to the
+// shared bound (one row of words each); scans with k <= kRowBoundMaxK use
+// it.
+constexpr int kRowBoundRows = 64;
+constexpr int kRowBoundMaxK = 16;
+// Words per bound row for C columns: whole 64-column tiles, so that a row of
+// a tile fills whole lines.
+inline int64_t row_bound_ld(int64_t C) { return (C + 63) / 64 * 64; }
 
 // One sampled draft per column from its top-k list (values sorted largest
 // first, C*k of the dtype; ids C*k): out_ids[c] = ids[c*k + j*], out_pos[c] =

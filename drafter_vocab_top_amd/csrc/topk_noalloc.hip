@@ -10,8 +10,8 @@
 //   [0, 256)                 the error word of a merging workgroup's wait
 //   tickets                  one 128-byte line per column (column layout):
 //                            zero between calls
-//   bound slots              16 words per column (row layout): zero between
-//                            calls (the row merge kernel clears them)
+//   bound words              up to 64 words per column (row layout): zero
+//                            between calls (the row merge kernel clears them)
 //   lists                    the partial lists of either layout.  Column
 //                            lists are tagged 1 and the column's merger sets
 //                            them back to zero; row lists are rewritten in
@@ -33,7 +33,7 @@ namespace {
 constexpr size_t kScratchBytes = size_t(8) << 20;
 constexpr int64_t kNoallocMaxColumns = 4096;
 constexpr size_t kTicketRegion = (size_t)kNoallocMaxColumns * kTicketStride * sizeof(uint32_t);
-constexpr size_t kBoundRegion = (size_t)kNoallocMaxColumns * kRowBoundSlots * sizeof(uint32_t);
+constexpr size_t kBoundRegion = (size_t)kNoallocMaxColumns * kRowBoundRows * sizeof(uint32_t);
 constexpr int kMaxDevices = 64;
 
 __device__ __align__(256) uint8_t scratch[kScratchBytes];

@@ -131,6 +131,7 @@ struct RowShared {
     uint32_t thr[TW];                            // running threshold per column (order)
     uint32_t cnt[TW];                            // candidates per column (may exceed CAP)
     uint32_t flag[TW];                           // 1: candidates overflowed, 2: negative NaN seen
+    uint32_t cm[TW];                             // first-pass maximum per column (order)
     uint32_t ovf;                                // some column overflowed in this pass
 };
 
@@ -315,11 +316,15 @@ __device__ __forceinline__ uint32_t group_min(uint32_t v) {
 
 // The k-th largest of the values a thread group holds (VPT per thread, empty
 // slots 0), by bisection of [lo, hi] where at least k values are >= lo and
-// hi is the largest value: about log2(hi - lo) counting rounds.
+// hi is the largest value: about log2(hi - lo) counting rounds.  The upper
+// midpoint is lo + ceil((hi - lo) / 2), written so that it does not wrap
+// when hi - lo is 2^32 - 1 (lo = 0 and a NaN, order 0xFFFFFFFF): a wrapped
+// midpoint equals lo and the bisection would never end.
 template <int TPC, int VPT>
 __device__ __forceinline__ uint32_t group_kth(const uint32_t (&v)[VPT], uint32_t k, uint32_t lo, uint32_t hi) {
     while (lo < hi) {
-        const uint32_t mid = lo + (hi - lo + 1u) / 2u;
+        const uint32_t d = hi - lo;
+        const uint32_t mid = lo + (d >> 1) + (d & 1u);
         uint32_t m = 0;
 #pragma unroll
         for (int j = 0; j < VPT; ++j) m += v[j] >= mid ? 1u : 0u;
@@ -541,6 +546,7 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
         sh.thr[tid] = 0;
         sh.cnt[tid] = 0;
         sh.flag[tid] = 0;
+        sh.cm[tid] = 0;
     }
     if (tid == 0) sh.ovf = 0;
 
@@ -641,15 +647,43 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
     };
     const u32x4 fill4 = u32x4{DT::kFillDword, DT::kFillDword, DT::kFillDword, DT::kFillDword};
 
-    // Lower bound shared by the segments of a column: slot j holds the
-    // largest group maximum published so far by a segment s with s mod k = j
-    // (zero if none yet).  Distinct slots hold elements of distinct segments,
-    // so once all k slots are filled their minimum is at most the column's
+    // Lower bound shared by the segments of a column: each segment s <
+    // kRowBoundRows stores one element of each of its columns (its largest
+    // group maximum) in row s of the bound area (bound_ld words a row).  A
+    // wave's stores fill whole lines that no other workgroup writes: loads
+    // of words that many workgroups write at once (atomics, or stores to
+    // one line) wait behind those writes for microseconds.  Distinct
+    // segments hold distinct elements, so the k-th largest of a column's
+    // words (zero where no segment has stored yet) is at most the column's
     // k-th largest order over all V rows: no element below it can be in the
-    // output, whatever segment it lies in.  The merge kernel zeroes the slots
-    // for the next run.
-    constexpr int kBoundPerThread = kRowBoundSlots / TPC;
-    const uint32_t* bound_col = a.bound + (int64_t)min_u32(c0 + pcol, C - 1u) * kRowBoundSlots;
+    // output, whatever segment it lies in.  The merge kernel zeroes the
+    // words for the next run.
+    constexpr int kBoundPerThread = kRowBoundRows / TPC;
+    const uint32_t bld = (uint32_t)a.bound_ld;
+    // 32-bit word indices from the area's base (the area is far below 2^32
+    // words): one register per thread, the rows' steps are uniform
+    const uint32_t bound_i = min_u32(c0 + pcol, C - 1u) + pq * (uint32_t)kBoundPerThread * bld;
+    auto load_bound = [&](uint32_t(&w)[kBoundPerThread]) {
+        // opaque here, so that the addresses are formed at each read rather
+        // than kept in registers across the pass loop
+        uint32_t bi = bound_i;
+        asm volatile("" : "+v"(bi));
+#pragma unroll
+        for (int j = 0; j < kBoundPerThread; ++j)
+            w[j] = __hip_atomic_load(&a.bound[bi + (uint32_t)j * bld], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    // max(floor, the k-th largest word): the bisection only searches above
+    // the threshold already known, a far narrower range than all the words'
+    auto bound_kth = [&](const uint32_t(&w)[kBoundPerThread], uint32_t floor) {
+        uint32_t wmax = w[0], n = 0;
+#pragma unroll
+        for (int j = 0; j < kBoundPerThread; ++j) {
+            wmax = max_u32(wmax, w[j]);
+            n += w[j] >= floor ? 1u : 0u;
+        }
+        if (group_sum<TPC>(n) < k) return floor;
+        return group_kth<TPC, kBoundPerThread>(w, k, floor, group_max<TPC>(wmax));
+    };
 
     uint32_t nanacc[4] = {0u, 0u, 0u, 0u};
     auto scan_passes = [&](auto full_tag) {
@@ -664,13 +698,16 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
     __syncthreads();
 
     for (uint32_t p = 0; p < npass; ++p) {
-        // the column's shared slots, read before the prefetch so that waiting
-        // for them does not wait for the next pass
-        uint32_t slot[kBoundPerThread];
-#pragma unroll
-        for (int j = 0; j < kBoundPerThread; ++j)
-            slot[j] = __hip_atomic_load(&bound_col[pq * kBoundPerThread + (uint32_t)j], __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
+        // The shared bound is read twice.  The first pass stores this
+        // segment's maxima as soon as its data is in, reads the bound back
+        // while it works out its starting thresholds, and filters against
+        // both.  The second pass reads it again at its top (by then nearly
+        // every segment has stored; the loads go before the prefetch, so
+        // that waiting for them does not wait for it) and applies it at its
+        // end, where the pass's filter has hidden the loads' latency.
+        const bool bound_late = a.use_bound && p == 1u && npass > 2u;
+        uint32_t bw[kBoundPerThread];
+        if (bound_late) load_bound(bw);
         if constexpr (FULL) {
             const bool more = p + 1 < npass;
             load_full(nxt, more ? p + 1 : 0u, more ? (uint32_t)kRowsPerStep : 0u);
@@ -694,6 +731,17 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
             for (int i = 0; i < NV; i += 2) {
                 m0.add(row_vec(cur[i], 0u, i));
                 m1.add(row_vec(cur[i + 1], 0u, i + 1));
+            }
+            if (a.use_bound) {
+                // the first pass's maximum of each column (an element of the
+                // segment) for the other segments, then the bound read back
+#pragma unroll
+                for (int j = 0; j < CPV; ++j) atomicMax(&sh.cm[g * CPV + j], max_u32(m0.order(j), m1.order(j)));
+                __syncthreads();
+                if (pq == 0 && c0 + pcol < C && s < (uint32_t)kRowBoundRows)
+                    __hip_atomic_store(&a.bound[s * bld + c0 + pcol], sh.cm[pcol], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                load_bound(bw);
             }
             if (npass > 1) {  // the second pass is already loaded: group maxima over both
 #pragma unroll
@@ -720,17 +768,19 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
             }
             // all 64 are >= the minimum, and k <= 64
             const uint32_t cmax = group_max<TPC>(vmax);
-            const uint32_t T = group_kth<TPC, RPT>(v, k, group_min<TPC>(vmin), cmax);
+            uint32_t T = group_kth<TPC, RPT>(v, k, group_min<TPC>(vmin), cmax);
+            if (a.use_bound) T = bound_kth(bw, T);
             if (pq == 0) {
                 uint32_t fmv, fqv;
                 F::encode(T, fmv, fqv);
                 sh.thr[pcol] = T;
                 sh.fm[pcol] = (storage)fmv;
                 sh.fq[pcol] = (storage)fqv;
-                // publish an element of this segment (at least as large as cmax) in slot s mod k
-                if (a.use_bound && c0 + pcol < C)
-                    __hip_atomic_fetch_max(&a.bound[(c0 + pcol) * kRowBoundSlots + s % k], cmax, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
+                // a larger element of the segment (over both passes) for the
+                // segments that read the bound later
+                if (a.use_bound && c0 + pcol < C && s < (uint32_t)kRowBoundRows && cmax > sh.cm[pcol])
+                    __hip_atomic_store(&a.bound[s * bld + c0 + pcol], cmax, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
             }
             __syncthreads();
         }
@@ -833,25 +883,22 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
                     }
                 }
             }
-            // the shared bound, once every one of the k slots is filled
-            uint32_t bmin = 0xFFFFFFFFu;
-#pragma unroll
-            for (int j = 0; j < kBoundPerThread; ++j)
-                if (pq * kBoundPerThread + (uint32_t)j < k) bmin = min_u32(bmin, slot[j]);
-            const uint32_t Tg = group_min<TPC>(bmin);
-            // (an overflowed column is left to the rebuild below; the bound
-            // applies to it from the next pass on)
-            if (a.use_bound && p + 1 < npass && Tg > sh.thr[pcol] && sh.cnt[pcol] <= (uint32_t)CAP) {
-                // candidates below the raised threshold can go at once
-                const uint32_t nc = sh.cnt[pcol];
-                const uint32_t kept = cull_column<DT, KT>(sh.cand[pcol], pq, nc, Tg);
-                if (pq == 0) {
-                    uint32_t fmv, fqv;
-                    F::encode(Tg, fmv, fqv);
-                    sh.thr[pcol] = Tg;
-                    sh.fm[pcol] = (storage)fmv;
-                    sh.fq[pcol] = (storage)fqv;
-                    sh.cnt[pcol] = kept;
+            // the shared bound read at the top of the second pass;
+            // candidates below it go at once (an overflowed column is left
+            // to the rebuild below; the bound applies to it from the next
+            // pass on)
+            if (bound_late) {
+                const uint32_t Tb = bound_kth(bw, sh.thr[pcol]);
+                if (Tb > sh.thr[pcol] && sh.cnt[pcol] <= (uint32_t)CAP) {
+                    const uint32_t kept = cull_column<DT, KT>(sh.cand[pcol], pq, sh.cnt[pcol], Tb);
+                    if (pq == 0) {
+                        uint32_t fmv, fqv;
+                        F::encode(Tb, fmv, fqv);
+                        sh.thr[pcol] = Tb;
+                        sh.fm[pcol] = (storage)fmv;
+                        sh.fq[pcol] = (storage)fqv;
+                        sh.cnt[pcol] = kept;
+                    }
                 }
             }
             // sh.ovf was set before the barrier that ended (2), so every
@@ -950,9 +997,9 @@ __global__ __launch_bounds__(kBlock) void topk_row_merge(RowArgs a) {
     const uint32_t k = (uint32_t)a.k, S = (uint32_t)a.S, M = S * k;
     const uint64_t* src = a.partials + (int64_t)col * M;
     if (threadIdx.x == 0) ncand = 0;
-    // the scan is over: clear the column's shared-bound slots for the next run
-    if (wave == 0 && a.use_bound && lane < (uint32_t)kRowBoundSlots)
-        a.bound[(int64_t)col * kRowBoundSlots + lane] = 0u;
+    // the scan is over: clear the column's shared-bound words for the next run
+    if (a.use_bound && threadIdx.x < (uint32_t)kRowBoundRows)
+        a.bound[(size_t)threadIdx.x * (uint32_t)a.bound_ld + col] = 0u;
     uint64_t keys[KW];
 #pragma unroll
     for (int j = 0; j < KW; ++j) {
