@@ -697,17 +697,18 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
     }
     __syncthreads();
 
+    // The shared bound is read twice.  The first pass stores this segment's
+    // maxima as soon as its data is in, reads the bound back while it works
+    // out its starting thresholds, and filters against both.  The second
+    // pass reads it again at its top (by then nearly every segment has
+    // stored; the loads go before the prefetch, so that waiting for them
+    // does not wait for it), and the third applies it at its end: two
+    // passes' filtering hide the loads' latency, which is several
+    // microseconds while every workgroup streams.
+    uint32_t bw[kBoundPerThread];
     for (uint32_t p = 0; p < npass; ++p) {
-        // The shared bound is read twice.  The first pass stores this
-        // segment's maxima as soon as its data is in, reads the bound back
-        // while it works out its starting thresholds, and filters against
-        // both.  The second pass reads it again at its top (by then nearly
-        // every segment has stored; the loads go before the prefetch, so
-        // that waiting for them does not wait for it) and applies it at its
-        // end, where the pass's filter has hidden the loads' latency.
-        const bool bound_late = a.use_bound && p == 1u && npass > 2u;
-        uint32_t bw[kBoundPerThread];
-        if (bound_late) load_bound(bw);
+        const bool bound_late = a.use_bound && p == 2u && npass > 3u;
+        if (a.use_bound && p == 1u && npass > 3u) load_bound(bw);
         if constexpr (FULL) {
             const bool more = p + 1 < npass;
             load_full(nxt, more ? p + 1 : 0u, more ? (uint32_t)kRowsPerStep : 0u);
@@ -997,9 +998,14 @@ __global__ __launch_bounds__(kBlock) void topk_row_merge(RowArgs a) {
     const uint32_t k = (uint32_t)a.k, S = (uint32_t)a.S, M = S * k;
     const uint64_t* src = a.partials + (int64_t)col * M;
     if (threadIdx.x == 0) ncand = 0;
-    // the scan is over: clear the column's shared-bound words for the next run
-    if (a.use_bound && threadIdx.x < (uint32_t)kRowBoundRows)
-        a.bound[(size_t)threadIdx.x * (uint32_t)a.bound_ld + col] = 0u;
+    // The scan is over: clear the shared-bound words for the next run.  Row
+    // r of the area is cleared by workgroup r mod C, in whole lines.
+    if (a.use_bound) {
+        for (uint32_t r = col; r < (uint32_t)kRowBoundRows; r += (uint32_t)a.C) {
+            uint32_t* row = a.bound + (size_t)r * (uint32_t)a.bound_ld;
+            for (uint32_t c = threadIdx.x; c < (uint32_t)a.C; c += kBlock) row[c] = 0u;
+        }
+    }
     uint64_t keys[KW];
 #pragma unroll
     for (int j = 0; j < KW; ++j) {
