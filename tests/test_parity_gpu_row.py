@@ -200,3 +200,37 @@ def test_merge_candidate_counts(gpu):
         x[rows, c] = big
     print(f"[parity-row] merge candidate counts 30/150/600, V={V} C={C} k={k}", flush=True)
     assert_parity(gpu, x, V, C, k, W.BF16, W.ROW, C, label="row merge candidate counts")
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+def test_nan_columns_with_shared_bound(gpu, dtype):
+    """NaNs at the full row count, with several passes per segment and more
+    than k segments (128 at this shape), so both reads of the shared bound
+    see them.  A column with positive NaNs in the first pass of more than k
+    segments makes the bound itself the NaN order (0xFFFF or 0xFFFFFFFF)
+    while words of segments that have not stored are still zero: the
+    bisection then spans the whole order range.
+    Negative NaNs send their segments to the exact path."""
+    V, C, k = 248046, 64, 16
+    x = W.random_matrix(6262, V, C, dtype, W.ROW)
+    b = x.view(np.uint16 if dtype == W.BF16 else np.uint32)
+    rng = np.random.default_rng(6263)
+    if dtype == W.BF16:
+        nan_pos, nan_neg, inf_pos, inf_neg = 0x7FC1, 0xFFC0, 0x7F80, 0xFF80
+    else:
+        nan_pos, nan_neg, inf_pos, inf_neg = 0x7FFFFFFF, 0xFFC00000, 0x7F800000, 0xFF800000
+    for c in range(C):
+        kind = c % 5
+        if kind == 0:      # positive NaNs near the start of 40 of the 128 segments, and elsewhere
+            b[[V * sg // 128 + 1 for sg in range(40)], c] = nan_pos
+            b[rng.choice(V, 20, replace=False), c] = nan_pos
+        elif kind == 1:    # a few negative NaNs
+            b[rng.choice(V, 5, replace=False), c] = nan_neg
+        elif kind == 2:    # both signs
+            b[rng.choice(V, 20, replace=False), c] = nan_pos
+            b[rng.choice(V, 20, replace=False), c] = nan_neg
+        elif kind == 3:    # infinities
+            b[rng.choice(V, 3, replace=False), c] = inf_pos
+            b[rng.choice(V, 3000, replace=False), c] = inf_neg
+    print(f"[parity-row] NaN columns with the shared bound, V={V} C={C} k={k} {dtype}", flush=True)
+    assert_parity(gpu, x, V, C, k, dtype, W.ROW, C, label=f"row NaN columns shared bound {dtype}")
