@@ -77,7 +77,7 @@ constexpr int kRowSmallK = 16;
 // Row segments below kRowBoundRows store one element per column to the
 // shared bound (one row of words each); scans with k <= kRowBoundMaxK use
 // it.
-constexpr int kRowBoundRows = 64;
+constexpr int kRowBoundRows = 32;
 constexpr int kRowBoundMaxK = 16;
 // Words per bound row for C columns: whole 64-column tiles, so that a row of
 // a tile fills whole lines.

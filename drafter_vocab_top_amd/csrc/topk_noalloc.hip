@@ -10,7 +10,7 @@
 //   [0, 256)                 the error word of a merging workgroup's wait
 //   tickets                  one 128-byte line per column (column layout):
 //                            zero between calls
-//   bound words              up to 64 words per column (row layout): zero
+//   bound words              32 words per column (row layout): zero
 //                            between calls (the row merge kernel clears them)
 //   lists                    the partial lists of either layout.  Column
 //                            lists are tagged 1 and the column's merger sets

@@ -769,8 +769,20 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
             }
             // all 64 are >= the minimum, and k <= 64
             const uint32_t cmax = group_max<TPC>(vmax);
-            uint32_t T = group_kth<TPC, RPT>(v, k, group_min<TPC>(vmin), cmax);
-            if (a.use_bound) T = bound_kth(bw, T);
+            // The starting threshold: the bound where it holds (almost every
+            // column), above the smallest group maximum (a valid threshold
+            // by itself: 64 >= k elements reach it); the local k-th group
+            // maximum only for the waves where some column has no bound yet.
+            // (The local search is VALU work that the workgroups on a CU
+            // would otherwise all do at once while the bound is in flight.)
+            const uint32_t vlo = group_min<TPC>(vmin);
+            uint32_t T;
+            if (a.use_bound) {
+                T = bound_kth(bw, vlo);
+                if (__ballot(T <= vlo) != 0ull) T = max_u32(T, group_kth<TPC, RPT>(v, k, vlo, cmax));
+            } else {
+                T = group_kth<TPC, RPT>(v, k, vlo, cmax);
+            }
             if (pq == 0) {
                 uint32_t fmv, fqv;
                 F::encode(T, fmv, fqv);

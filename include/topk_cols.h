@@ -71,7 +71,7 @@ typedef struct topk_cols *topk_cols_t;
  * keys per column and vocabulary segment (C * segments * k keys), an error
  * word and, for the column-contiguous layout, one 128-byte line per column
  * holding a counter and the run count modulo 255, or, for the
- * row-interleaved layout, 64 4-byte bound words per column (C rounded up to
+ * row-interleaved layout, 32 4-byte bound words per column (C rounded up to
  * a multiple of 64) that the segments of a column share during a run.  Create allocates it on the
  * current device with hipMalloc, zeroes it and waits for the zeroing to
  * finish; create is not meant for the hot loop.  Every run leaves the
@@ -232,7 +232,7 @@ const char *topk_cols_status_string(int status);
  *
  * Returns the errors of topk_cols_create for a bad shape, and
  * TOPK_ERR_UNSUPPORTED when C > 4096 or the shape's workspace exceeds the
- * array (for example 248,046 x 448 bf16 rows with k = 16 needs 7.5 MiB and
+ * array (for example 248,046 x 448 bf16 rows with k = 16 needs 7.0 MiB and
  * fits); TOPK_ERR_INVALID_ARG for a NULL or misaligned pointer;
  * TOPK_ERR_HIP when there is no device or the launch fails.
  */
