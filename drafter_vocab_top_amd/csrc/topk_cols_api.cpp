@@ -92,7 +92,9 @@ int make_plan(Plan* plan, int64_t V, int64_t C, int32_t k, int32_t dtype, int32_
     if (row && algo != TOPK_ALGO_AUTO) return TOPK_ERR_UNSUPPORTED;
     if (row && forced_segments * k > kRowMaxMergeKeys) return TOPK_ERR_UNSUPPORTED;
     if (algo == TOPK_ALGO_ONE_WAVE && forced_segments > 1) return TOPK_ERR_UNSUPPORTED;  // no split
-    if (C > 0x7FFFFFFF || (row && row_bound_ld(C) > 0x7FFFFFFF)) return TOPK_ERR_UNSUPPORTED;
+    if (C > 0x7FFFFFFF) return TOPK_ERR_UNSUPPORTED;
+    // the row scan indexes the shared-bound area with 32-bit word indices
+    if (row && row_bound_ld(C) * kRowBoundRows > 0xFFFFFFFFll) return TOPK_ERR_UNSUPPORTED;
     if (cu_count < 1) return TOPK_ERR_HIP;
 
     if (!row && algo == TOPK_ALGO_AUTO) algo = TOPK_ALGO_WORKGROUP;

@@ -660,8 +660,8 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
     // words for the next run.
     constexpr int kBoundPerThread = kRowBoundRows / TPC;
     const uint32_t bld = (uint32_t)a.bound_ld;
-    // 32-bit word indices from the area's base (the area is far below 2^32
-    // words): one register per thread, the rows' steps are uniform
+    // 32-bit word indices from the area's base (plans keep the area below
+    // 2^32 words): one register per thread, the rows' steps are uniform
     const uint32_t bound_i = min_u32(c0 + pcol, C - 1u) + pq * (uint32_t)kBoundPerThread * bld;
     auto load_bound = [&](uint32_t(&w)[kBoundPerThread]) {
         // opaque here, so that the addresses are formed at each read rather
@@ -672,8 +672,9 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
         for (int j = 0; j < kBoundPerThread; ++j)
             w[j] = __hip_atomic_load(&a.bound[bi + (uint32_t)j * bld], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
-    // max(floor, the k-th largest word): the bisection only searches above
-    // the threshold already known, a far narrower range than all the words'
+    // max(floor, the k-th largest word), for a floor that is already a
+    // valid threshold: the bisection only searches above it, a far narrower
+    // range than all the words'
     auto bound_kth = [&](const uint32_t(&w)[kBoundPerThread], uint32_t floor) {
         uint32_t wmax = w[0], n = 0;
 #pragma unroll
@@ -698,8 +699,9 @@ __global__ __launch_bounds__(kBlock) void topk_row_scan(RowArgs a) {
     __syncthreads();
 
     // The shared bound is read twice.  The first pass stores this segment's
-    // maxima as soon as its data is in, reads the bound back while it works
-    // out its starting thresholds, and filters against both.  The second
+    // maxima as soon as its data is in, reads the bound back while it
+    // gathers the second pass's group maxima, and filters against it (where
+    // it does not hold yet, against the local k-th group maximum).  The second
     // pass reads it again at its top (by then nearly every segment has
     // stored; the loads go before the prefetch, so that waiting for them
     // does not wait for it), and the third applies it at its end: two

@@ -79,7 +79,8 @@ typedef struct topk_cols *topk_cols_t;
  *
  * On any failure *out is set to NULL, and nothing stays allocated.
  * Returns TOPK_ERR_INVALID_ARG for a bad argument or a NULL out.
- * Returns TOPK_ERR_UNSUPPORTED when k > TOPK_MAX_K or V > TOPK_MAX_V.
+ * Returns TOPK_ERR_UNSUPPORTED when k > TOPK_MAX_K or V > TOPK_MAX_V, or
+ * for the row-interleaved layout when C > 134,217,664.
  * Returns TOPK_ERR_HIP when there is no usable device.
  * Returns TOPK_ERR_OUT_OF_MEMORY when the allocation fails.
  */

@@ -72,6 +72,7 @@ def _create(lib, *args, segments=None):
     ((10, 7, 1, 0, 1, 6), T.TOPK_ERR_INVALID_ARG),           # ld < C (row-interleaved)
     ((100, 7, 65, 0, 0, 100), T.TOPK_ERR_UNSUPPORTED),       # k > TOPK_MAX_K
     ((1 << 24, 7, 8, 0, 0, 1 << 24), T.TOPK_ERR_UNSUPPORTED),  # V > TOPK_MAX_V
+    ((10, 1 << 27, 1, 0, 1, 1 << 27), T.TOPK_ERR_UNSUPPORTED),  # row bound area past 2^32 words
 ])
 def test_invalid_arguments_refused_without_a_device(lib, args, expect):
     rc, h = _create(lib, *args)
