@@ -234,3 +234,26 @@ def test_nan_columns_with_shared_bound(gpu, dtype):
             b[rng.choice(V, 3000, replace=False), c] = inf_neg
     print(f"[parity-row] NaN columns with the shared bound, V={V} C={C} k={k} {dtype}", flush=True)
     assert_parity(gpu, x, V, C, k, dtype, W.ROW, C, label=f"row NaN columns shared bound {dtype}")
+
+
+def test_random_shapes_with_shared_bound(gpu):
+    """Seeded random shapes around the shared bound's cases: k <= 16 (the
+    bound in use), segment counts on both sides of its 32 publishing
+    segments and of k, one to several passes per segment, partial column
+    tiles, padded rows and every value kind."""
+    rng = np.random.default_rng(7070)
+    kinds = ["normal", "alphabet", "special", "equal", "normal", "normal"]
+    for case in range(24):
+        dtype = (W.BF16, W.F32)[case % 2]
+        kind = kinds[case % len(kinds)]
+        V = int(rng.integers(300, 120001))
+        C = int(rng.integers(1, 140))
+        k = int(rng.integers(1, 17))
+        k = min(k, V)
+        seg = int(rng.choice([0, 0, k, max(k, 17), max(k, 31), max(k, 33), max(k, 64), 2048 // k]))
+        seg = min(seg, 2048 // k)
+        ld = C + int(rng.integers(0, 3))
+        x = W.random_matrix(9000 + case, V, C, dtype, W.ROW, ld=ld, kind=kind)
+        print(f"[parity-row] random case {case}: V={V} C={C} k={k} {dtype} {kind} segments={seg} ld={ld}", flush=True)
+        assert_parity(gpu, x, V, C, k, dtype, W.ROW, ld, segments=seg,
+                      label=f"row random case {case} V={V} C={C} k={k} seg={seg}")
