@@ -498,6 +498,17 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
             const uint32_t r = lds_rank_of(sh.cand, n8, key);
             if (lane < n_last && r < k)
                 __hip_atomic_store(&dst[r], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else if (n_last <= 128u) {
+            // two candidates per lane (common at k = 20): one pass ranks both
+            const uint32_t n8 = (n_last + 7u) & ~7u;
+            uint64_t ka = sh.cand[lane], kb = 0;
+            if (lane + 64u < n_last) kb = sh.cand[lane + 64u];
+            else if (lane + 64u < n8) sh.cand[lane + 64u] = 0;  // padding for the rank
+            uint32_t ra, rb;
+            lds_rank2_of(sh.cand, n8, ka, kb, ra, rb);
+            if (ra < k) __hip_atomic_store(&dst[ra], ka, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane + 64u < n_last && rb < k)
+                __hip_atomic_store(&dst[rb], kb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         } else {
             const uint32_t m = wave_rank_select(sh.cand, n_last, k, sh.best);
             if (lane < m) __hip_atomic_store(&dst[lane], sh.best[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
