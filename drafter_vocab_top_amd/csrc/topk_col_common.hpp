@@ -112,4 +112,24 @@ __device__ __forceinline__ uint32_t wave_kth_bound(uint32_t order, uint32_t k) {
     else return wave_kth_largest<16>(order >> 16, k) << 16;
 }
 
+// Rank of two keys per lane among n <= 128 LDS keys (key a for slot lane,
+// key b for slot lane + 64; n8 is n rounded up to 8, the padding zero): one
+// pass over the keys counts, for both, how many are larger.
+__device__ __forceinline__ void lds_rank2_of(const uint64_t* keys, uint32_t n8, uint64_t a, uint64_t b,
+                                             uint32_t& ra, uint32_t& rb) {
+    uint32_t a0 = 0, a1 = 0, b0 = 0, b1 = 0;
+    for (uint32_t j = 0; j < n8; j += 8) {
+        const u64x2 q0 = *reinterpret_cast<const u64x2*>(keys + j);
+        const u64x2 q1 = *reinterpret_cast<const u64x2*>(keys + j + 2);
+        const u64x2 q2 = *reinterpret_cast<const u64x2*>(keys + j + 4);
+        const u64x2 q3 = *reinterpret_cast<const u64x2*>(keys + j + 6);
+        a0 += (uint32_t)(q0.x > a) + (uint32_t)(q0.y > a) + (uint32_t)(q1.x > a) + (uint32_t)(q1.y > a);
+        a1 += (uint32_t)(q2.x > a) + (uint32_t)(q2.y > a) + (uint32_t)(q3.x > a) + (uint32_t)(q3.y > a);
+        b0 += (uint32_t)(q0.x > b) + (uint32_t)(q0.y > b) + (uint32_t)(q1.x > b) + (uint32_t)(q1.y > b);
+        b1 += (uint32_t)(q2.x > b) + (uint32_t)(q2.y > b) + (uint32_t)(q3.x > b) + (uint32_t)(q3.y > b);
+    }
+    ra = a0 + a1;
+    rb = b0 + b1;
+}
+
 }  // namespace topk

@@ -235,25 +235,6 @@ __device__ __forceinline__ uint32_t lds_rank_of(const uint64_t* keys, uint32_t n
     return r0 + r1;
 }
 
-// The same for n <= 128 keys, two per lane (key a and key b, for slots lane
-// and lane + 64): one pass over the LDS keys ranks both.
-__device__ __forceinline__ void lds_rank2_of(const uint64_t* keys, uint32_t n8, uint64_t a, uint64_t b,
-                                             uint32_t& ra, uint32_t& rb) {
-    uint32_t a0 = 0, a1 = 0, b0 = 0, b1 = 0;
-    for (uint32_t j = 0; j < n8; j += 8) {
-        const u64x2 q0 = *reinterpret_cast<const u64x2*>(keys + j);
-        const u64x2 q1 = *reinterpret_cast<const u64x2*>(keys + j + 2);
-        const u64x2 q2 = *reinterpret_cast<const u64x2*>(keys + j + 4);
-        const u64x2 q3 = *reinterpret_cast<const u64x2*>(keys + j + 6);
-        a0 += (uint32_t)(q0.x > a) + (uint32_t)(q0.y > a) + (uint32_t)(q1.x > a) + (uint32_t)(q1.y > a);
-        a1 += (uint32_t)(q2.x > a) + (uint32_t)(q2.y > a) + (uint32_t)(q3.x > a) + (uint32_t)(q3.y > a);
-        b0 += (uint32_t)(q0.x > b) + (uint32_t)(q0.y > b) + (uint32_t)(q1.x > b) + (uint32_t)(q1.y > b);
-        b1 += (uint32_t)(q2.x > b) + (uint32_t)(q2.y > b) + (uint32_t)(q3.x > b) + (uint32_t)(q3.y > b);
-    }
-    ra = a0 + a1;
-    rb = b0 + b1;
-}
-
 // Rank selection by one wave (see rank_select).
 __device__ __forceinline__ uint32_t wave_rank_select(const uint64_t* keys, uint32_t n, uint32_t k,
                                                      uint64_t* out) {
