@@ -20,10 +20,12 @@ OBJDIR = os.path.join(ROOT, "_build")
 # Per-source flags.  The column kernel takes its ticket before ranking and
 # publishing its list and reads the reply afterwards; the compiler's atomic
 # optimizer would otherwise wait for the reply right after the atomic (it
-# broadcasts the returned value at once), so it is off for that file.  The
+# broadcasts the returned value at once), so it is off for that file.  Its
+# kernel's leading scalar arguments are preloaded into registers.  The
 # row scan asks for three waves per SIMD, which its instantiations with the
 # larger candidate area cannot reach; the note saying so is silenced.
-EXTRA_FLAGS = {"topk_col.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
+EXTRA_FLAGS = {"topk_col.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
+                                 "-mllvm", "-amdgpu-kernarg-preload-count=16"],
                "topk_row.hip": ["-Wno-pass-failed"]}
 # A plain streaming-read kernel that the benchmark times beside the top-k (not
 # part of the top-k library).

@@ -281,8 +281,14 @@ __device__ __forceinline__ bool merge_lists_wave(const ColArgs& a, ColShared& sh
     return true;
 }
 
+// The fields the first loads need come first, as separate arguments, so that
+// the hardware can place them in registers as the waves start (kernarg
+// preload) instead of every workgroup reading them before its first load;
+// the rest follow in ColArgs.  Column c0 + blockIdx.y, segment blockIdx.x.
 template <class DT, int NV>
-__global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
+__global__ __launch_bounds__(kBlock) void topk_col_kernel(const void* x, int64_t ld, uint32_t V, uint32_t S,
+                                                          uint32_t seg_vecs, uint32_t c0, uint32_t* tickets,
+                                                          ColArgs a) {
     using storage = typename DT::storage;
     constexpr int EPV = DT::kPerVec;
     __shared__ ColShared sh;
@@ -291,16 +297,14 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
     const uint32_t k = (uint32_t)a.k;
     // Rows and vector indices fit in 32 bits (V < 2^24); only the column
     // offset c * ld needs 64.
-    const uint32_t S = (uint32_t)a.S;
-    const uint32_t c = blockIdx.x / S;
-    const uint32_t s = blockIdx.x - c * S;
-    const uint32_t V = (uint32_t)a.V;
-    const storage* col = static_cast<const storage*>(a.x) + (int64_t)c * a.ld;
+    const uint32_t c = c0 + blockIdx.y;
+    const uint32_t s = blockIdx.x;
+    const storage* col = static_cast<const storage*>(x) + (int64_t)c * ld;
     // The column's ticket and the run's tag share a 128-byte line: word 0
     // counts the workgroups that finished, word 1 holds the run count
     // modulo 255 (the tag is one more).  Read before any data load; the
     // read travels with the data.
-    uint32_t* ticket = a.tickets + c * kTicketStride;
+    uint32_t* ticket = tickets + c * kTicketStride;
     const uint32_t epoch_v = __hip_atomic_load(ticket + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint32_t epoch = 0, tag = 0;  // taken from epoch_v once the first pass's data are in
 
@@ -309,7 +313,7 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
     if (head > V) head = V;
     const uint32_t nvec = (V - head) / EPV;
     const uint32_t tail0 = head + nvec * EPV;
-    const uint32_t vb = nvec * s / S, ve = nvec * (s + 1) / S;
+    const uint32_t vb = min_u32(s * seg_vecs, nvec), ve = min_u32(vb + seg_vecs, nvec);
     const u32x4* vec = reinterpret_cast<const u32x4*>(col + head);
 
     // This lane's edge element (wave 0 only): its row, or all ones, and its
@@ -320,6 +324,30 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
     if (s == S - 1 && tid >= 32 && tid - 32 < V - tail0) edge_row = tail0 + (tid - 32);
     uint32_t edge_raw = 0;
     if (edge_row != 0xFFFFFFFFu) edge_raw = (uint32_t)col[edge_row];
+
+    // A pass's vectors (fill values past the segment's end).  The first
+    // pass's loads go out here, before the loop's set-up, and the LDS init's
+    // barrier waits while they are in flight.  With 8 vectors per lane the
+    // loads are unconditional (a slot past the end re-reads the segment's
+    // last vector) and the fill is chosen when the pass uses them: cheaper
+    // than a branch per load there, dearer with fewer (measured).
+    u32x4 d[NV];
+    auto load_pass = [&](uint32_t v0) {
+        if constexpr (NV >= 8) {
+            if (ve > vb) {
+#pragma unroll
+                for (int i = 0; i < NV; ++i) d[i] = load_vec(vec + min_u32(v0 + (uint32_t)i * kBlock, ve - 1u));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const uint32_t vi = v0 + (uint32_t)i * kBlock;
+                d[i] = vi < ve ? load_vec(vec + vi)
+                               : u32x4{DT::kFillDword, DT::kFillDword, DT::kFillDword, DT::kFillDword};
+            }
+        }
+    };
+    load_pass(vb + tid);
     if (tid == 0) {
         sh.ncand = 0;
         sh.overflow = 0;
@@ -335,15 +363,14 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
 
     for (uint32_t p = 0; p < npass; ++p) {
         const uint32_t v0 = vb + p * per_pass + tid;
-        u32x4 d[NV];
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const uint32_t vi = v0 + (uint32_t)i * kBlock;
-            d[i] = vi < ve ? load_vec(vec + vi)
-                           : u32x4{DT::kFillDword, DT::kFillDword, DT::kFillDword, DT::kFillDword};
-        }
+        if (p > 0) load_pass(v0);
         // vector slots of this lane that hold data
         const int nvalid = ve > v0 ? (int)min_u32((uint32_t)NV, (ve - v0 + kBlock - 1) / kBlock) : 0;
+        if constexpr (NV >= 8) {
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                if (i >= nvalid) d[i] = u32x4{DT::kFillDword, DT::kFillDword, DT::kFillDword, DT::kFillDword};
+        }
         uint32_t vmax[NV];
         uint32_t rep;
         bool neg_nan;
@@ -553,16 +580,27 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(ColArgs a) {
     }
 }
 
+// One launch per kColGridY columns (the grid's y size is at most 65,535).
+template <class DT, int NV>
+hipError_t launch_nv(const ColArgs& a, hipStream_t stream) {
+    for (int64_t c0 = 0; c0 < a.C; c0 += kColGridY) {
+        const int64_t n = a.C - c0 < kColGridY ? a.C - c0 : kColGridY;
+        hipLaunchKernelGGL((topk_col_kernel<DT, NV>), dim3((uint32_t)a.S, (uint32_t)n), dim3(kBlock), 0, stream,
+                           a.x, a.ld, (uint32_t)a.V, (uint32_t)a.S, a.seg_vecs, (uint32_t)c0, a.tickets, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 template <class DT>
 hipError_t launch_dt(int nv, const ColArgs& a, hipStream_t stream) {
-    const dim3 grid((uint32_t)((int64_t)a.C * a.S)), block(kBlock);
     switch (nv) {
-        case 2: hipLaunchKernelGGL((topk_col_kernel<DT, 2>), grid, block, 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((topk_col_kernel<DT, 4>), grid, block, 0, stream, a); break;
-        case 8: hipLaunchKernelGGL((topk_col_kernel<DT, 8>), grid, block, 0, stream, a); break;
+        case 2: return launch_nv<DT, 2>(a, stream);
+        case 4: return launch_nv<DT, 4>(a, stream);
+        case 8: return launch_nv<DT, 8>(a, stream);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace

@@ -159,6 +159,11 @@ hipError_t launch_plan(const Plan& h, void* ws, int64_t n_cols, const void* logi
     a.C = (int32_t)n_cols;
     a.k = h.k;
     a.S = (int32_t)h.segments;
+    // Segment s takes 16-byte vectors [s * seg_vecs, (s + 1) * seg_vecs) of
+    // its column, cut at the column's vector count (the last segments may
+    // hold fewer, or none); a column has at most V / (elements per vector).
+    const int64_t elements_per_vector = h.dtype == TOPK_BF16 ? 8 : 4;
+    a.seg_vecs = (uint32_t)ceil_div(h.V / elements_per_vector, h.segments);
     a.spin_limit = spin_limit;
     a.fail_waits = fail_waits;
     a.clear_lists = clear_lists;

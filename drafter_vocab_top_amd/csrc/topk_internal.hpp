@@ -18,6 +18,7 @@ struct ColArgs {
     int32_t C;
     int32_t k;
     int32_t S;            // vocabulary segments (workgroups) per column, <= kMaxSegments
+    uint32_t seg_vecs;    // 16-byte vectors per segment, ceil(floor(V / elements per vector) / S)
     uint32_t spin_limit;  // re-reads of a list slot before the merger gives up
     uint32_t fail_waits;  // tests only: the merger treats every list as not yet published
     uint32_t clear_lists; // 1: the workspace is shared between shapes (keep tag 1, zero the lists after a run)
@@ -36,6 +37,8 @@ constexpr int kMaxSegments = 64;
 // Per-column tickets sit 128 bytes apart: counters of different columns in
 // one cache line serialize every workgroup's atomic on that line.
 constexpr int kTicketStride = 32;
+// Columns per launch of the column-contiguous kernel (the grid's y size).
+constexpr int64_t kColGridY = 65535;
 // 16-byte vectors per lane per pass: the kernel is instantiated for these.
 constexpr int kColVecChoices[3] = {2, 4, 8};
 

@@ -143,6 +143,17 @@ def test_negative_and_nan_columns(gpu, dtype):
             assert_parity(gpu, x, V, C, k, dtype, W.COL, V, segments=seg, label=f"neg/nan k={k} seg={seg}")
 
 
+def test_more_columns_than_one_grid_row(gpu):
+    """More columns than the launch grid's y size holds (65,535): the rest
+    continue along z.  Every column is checked, with the automatic split
+    and with two segments per column."""
+    V, C = 40, 70003
+    x = W.random_matrix(7003, V, C, W.BF16, W.COL, kind="normal")
+    for k, seg in ((3, 0), (3, 2)):
+        print(f"[parity] V={V} C={C} k={k} segments={seg}", flush=True)
+        assert_parity(gpu, x, V, C, k, W.BF16, W.COL, V, segments=seg, label=f"C={C} k={k} seg={seg}")
+
+
 def test_exhaustive_small_alphabet_columns(gpu):
     # Every length-6 column over {-inf, -1, -0, +0, 1}: 15,625 columns, every k.
     cols = W.exhaustive_columns([0xFF80, 0xBF80, 0x8000, 0x0000, 0x3F80], 6).astype(np.uint16)
