@@ -384,15 +384,21 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(const void* x, int64_t
             if (edge_row != 0xFFFFFFFFu) ex = make_key(DT::order((storage)edge_raw), edge_row, tag);
         }
         if (ex) rep = max_u32(rep, key_order(ex));
-        // Each wave's k-th largest lane maximum bounds the workgroup's k-th
-        // largest element from below, so the largest of the four does too.
-        // (For k = 1 a wave's own maximum already leaves only its ties.)
-        uint32_t T = wave_kth_bound<DT>(rep, k);
-        if (k > 1) {
+        // Each wave takes its kw-th largest lane maximum, kw = ceil(k / 4):
+        // every wave then holds at least kw elements at or above the smallest
+        // of the four, so that smallest bounds the workgroup's k-th largest
+        // element from below.  (For k = 1 a wave's own maximum already leaves
+        // only its ties.)
+        uint32_t T;
+        if (k == 1) {
+            T = wave_max_u32(rep);
+        } else {
+            const uint32_t kw = (k + kWaves - 1) / kWaves;
+            T = kw <= 2 ? wave_top12(rep, kw) : wave_kth_bound<DT>(rep, kw);
             if ((tid & 63u) == 0) sh.wave_thr[wave] = T;
             __syncthreads();
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) T = max_u32(T, sh.wave_thr[w]);
+            for (int w = 0; w < kWaves; ++w) T = min_u32(T, sh.wave_thr[w]);
         }
         if (nbest == k) T = max_u32(T, key_order(t_run));
         const uint64_t tc = max_u64((uint64_t)T << 32, nbest == k ? t_run + 1 : (uint64_t)0);

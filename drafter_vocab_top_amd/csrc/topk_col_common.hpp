@@ -132,4 +132,13 @@ __device__ __forceinline__ void lds_rank2_of(const uint64_t* keys, uint32_t n8, 
     rb = b0 + b1;
 }
 
+// The j-th largest of one value per lane, j = 1 or 2, by wave maxima: the
+// second is the maximum once one lane holding the first is set aside.
+__device__ __forceinline__ uint32_t wave_top12(uint32_t v, uint32_t j) {
+    const uint32_t m = wave_max_u32(v);
+    if (j == 1) return m;
+    const uint32_t first = (uint32_t)__builtin_ctzll(__ballot(v == m));
+    return wave_max_u32((threadIdx.x & 63u) == first ? 0u : v);
+}
+
 }  // namespace topk
