@@ -6,6 +6,8 @@
 
 #include <stdlib.h>
 
+#include <algorithm>
+
 #include <new>
 
 #include "topk_internal.hpp"
@@ -33,13 +35,16 @@ int element_size(int32_t dtype) { return dtype == TOPK_BF16 ? 2 : 4; }
 
 int64_t vectors_per_column(int64_t V, int dtype) { return V / (16 / element_size(dtype)); }
 
-int64_t choose_col_segments(int64_t V, int64_t C, int dtype, int cu_count) {
+int64_t choose_col_segments(int64_t V, int64_t C, int32_t k, int dtype, int cu_count) {
     const int64_t nvec = vectors_per_column(V, dtype);
     const int64_t max_nv = kColVecChoices[2];
     int64_t s = ceil_div(nvec, kBlockThreads * max_nv);                 // one pass per workgroup
-    // about one workgroup per CU: more segments make the merge longer than
-    // they make the scan shorter
-    const int64_t fill = ceil_div((int64_t)cu_count, C);
+    // Fill the CUs, but with at most one workgroup per CU (a CU that runs
+    // two holds up its columns' merges); for k > 1 also with no more
+    // segments than one pass of 4 vectors per lane needs, since the merge
+    // reads S*k keys.
+    int64_t fill = (int64_t)cu_count / C;
+    if (k > 1) fill = std::min(fill, ceil_div(nvec, kBlockThreads * kColVecChoices[1]));
     if (fill > s) s = fill;
     const int64_t most = nvec / kMinVecsPerSegment;                     // not too thin
     if (s > most) s = most;
@@ -103,7 +108,7 @@ int make_plan(Plan* plan, int64_t V, int64_t C, int32_t k, int32_t dtype, int32_
     const int64_t S = one_wave ? 1
                       : forced_segments > 0 ? forced_segments
                       : row ? choose_row_segments(V, tiles, k, cu_count)
-                            : choose_col_segments(V, C, dtype, cu_count);
+                            : choose_col_segments(V, C, k, dtype, cu_count);
     const int64_t blocks = row ? tiles * S : C * S;
     if (blocks > 0x7FFFFFFF) return TOPK_ERR_UNSUPPORTED;
 
