@@ -355,6 +355,7 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(const void* x, int64_t
     __syncthreads();
 
     uint64_t* wb = sh.wbuf[wave];
+    uint32_t old = 0;  // the ticket's reply (thread 0)
     uint32_t nbest = 0;  // the segment's best so far, in sh.cand[0..nbest) at the start of a pass
     uint64_t t_run = 0;  // the k-th best key once nbest == k
     uint32_t n_last = 0; // candidates of the last pass, in sh.cand
@@ -402,6 +403,10 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(const void* x, int64_t
         }
         if (nbest == k) T = max_u32(T, key_order(t_run));
         const uint64_t tc = max_u64((uint64_t)T << 32, nbest == k ? t_run + 1 : (uint64_t)0);
+        // The last pass takes the column's ticket as soon as its threshold
+        // is known; the reply is read only after the list is published, so
+        // the round trip hides the extraction and the rank.
+        if (p + 1 == npass && tid == 0) old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
         bool exact = __any(neg_nan);
         uint32_t cnt = 0;
@@ -511,18 +516,15 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(const void* x, int64_t
         }
     }
 
-    // ---- wave 0: take the column's ticket, rank the segment's candidates
-    //      and publish the sorted list; the list's slots carry the run tag,
-    //      so the last ticket holder waits for any list not yet published ----
+    // ---- wave 0: rank the segment's candidates and publish the sorted list
+    //      (the ticket was taken in the last pass); the list's slots carry
+    //      the run tag, so the last ticket holder waits for any list not yet
+    //      published ----
     const uint64_t sentinel = tag;  // order 0: below every real key
     uint64_t* parts = a.partials + (int64_t)c * S * k;
     if (wave == 0) {
         const uint32_t lane = tid;
         uint64_t* dst = parts + s * k;
-        // the ticket is taken first and its reply awaited only after the
-        // list is ranked and published: the round trip hides the rank
-        uint32_t old = 0;
-        if (lane == 0) old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (n_last <= 64u) {
             const uint32_t n8 = (n_last + 7u) & ~7u;
             uint64_t key = 0;
