@@ -327,10 +327,11 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(const void* x, int64_t
 
     // A pass's vectors (fill values past the segment's end).  The first
     // pass's loads go out here, before the loop's set-up, and the LDS init's
-    // barrier waits while they are in flight.  With 8 vectors per lane the
-    // loads are unconditional (a slot past the end re-reads the segment's
-    // last vector) and the fill is chosen when the pass uses them: cheaper
-    // than a branch per load there, dearer with fewer (measured).
+    // barrier waits while they are in flight.  With 8 or more vectors per
+    // lane the loads are unconditional (a slot past the end re-reads the
+    // segment's last vector) and the fill is chosen when the pass uses
+    // them: cheaper than a branch per load there, dearer with fewer
+    // (measured).
     u32x4 d[NV];
     auto load_pass = [&](uint32_t v0) {
         if constexpr (NV >= 8) {
@@ -607,6 +608,7 @@ hipError_t launch_dt(int nv, const ColArgs& a, hipStream_t stream) {
         case 2: return launch_nv<DT, 2>(a, stream);
         case 4: return launch_nv<DT, 4>(a, stream);
         case 8: return launch_nv<DT, 8>(a, stream);
+        case 16: return launch_nv<DT, 16>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -37,7 +37,7 @@ int64_t vectors_per_column(int64_t V, int dtype) { return V / (16 / element_size
 
 int64_t choose_col_segments(int64_t V, int64_t C, int32_t k, int dtype, int cu_count) {
     const int64_t nvec = vectors_per_column(V, dtype);
-    const int64_t max_nv = kColVecChoices[2];
+    const int64_t max_nv = kColVecChoices[3];
     int64_t s = ceil_div(nvec, kBlockThreads * max_nv);                 // one pass per workgroup
     // Fill the CUs, but with at most one workgroup per CU (a CU that runs
     // two holds up its columns' merges); for k > 1 also with no more
@@ -76,7 +76,7 @@ int choose_col_nv(int64_t V, int64_t S, int dtype) {
     const int64_t per_block = ceil_div(vectors_per_column(V, dtype), S);
     for (int nv : kColVecChoices)
         if (per_block <= kBlockThreads * nv) return nv;
-    return kColVecChoices[2];
+    return kColVecChoices[3];
 }
 
 }  // namespace

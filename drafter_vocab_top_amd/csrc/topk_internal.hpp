@@ -40,7 +40,7 @@ constexpr int kTicketStride = 32;
 // Columns per launch of the column-contiguous kernel (the grid's y size).
 constexpr int64_t kColGridY = 65535;
 // 16-byte vectors per lane per pass: the kernel is instantiated for these.
-constexpr int kColVecChoices[3] = {2, 4, 8};
+constexpr int kColVecChoices[4] = {2, 4, 8, 16};
 
 // dtype: TOPK_BF16 or TOPK_F32; nv: one of kColVecChoices.
 hipError_t launch_col(int dtype, int nv, const ColArgs& a, hipStream_t stream);
