@@ -74,7 +74,7 @@ constexpr int kWaveCap = 192;                // candidate slots per wave
 constexpr int kBlockCap = 512;               // carried best + candidates per workgroup
 constexpr int kMergeKeysPerThread = 16;      // S*k <= 4096 published keys, 16 per thread
 constexpr int kQueue = 128;                  // queued vectors per wave
-constexpr int kWaveMergeKeys = 1024;         // wave 0 alone merges up to this many published keys
+constexpr int kWaveMergeKeys = 256;          // wave 0 alone merges up to this many published keys
 
 struct ColShared {
     alignas(16) uint64_t cand[kBlockCap];          // [0, nbest) carried best, then candidates
@@ -225,11 +225,10 @@ __device__ __forceinline__ bool merge_lists(const ColArgs& a, ColShared& sh, con
 // maximum is the threshold, the keys at or above it are ranked (through
 // 16-byte LDS broadcasts when at most 64), and out(position, key) writes each of
 // the top k.
-template <class DT, class Out>
+template <class DT, int RMAX, class Out>
 __device__ __forceinline__ bool merge_lists_wave(const ColArgs& a, ColShared& sh, const uint64_t* parts,
                                                  uint32_t tag, const Out& out) {
     constexpr int OB = DT::kOrderBits;
-    constexpr int RMAX = kWaveMergeKeys / 64;
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t k = (uint32_t)a.k;
     const uint32_t M = (uint32_t)a.S * k;
@@ -568,7 +567,12 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(const void* x, int64_t
     uint32_t first, stride;
     if ((uint32_t)a.S * k <= (uint32_t)kWaveMergeKeys) {
         if (wave != 0) return;
-        ok = merge_lists_wave<DT>(a, sh, parts, tag, write_out);
+        // instantiated for the keys per lane the run needs: a larger
+        // instance costs its guarded slots even where they are empty
+        const uint32_t M = (uint32_t)a.S * k;
+        ok = M <= 64u    ? merge_lists_wave<DT, 1>(a, sh, parts, tag, write_out)
+             : M <= 128u ? merge_lists_wave<DT, 2>(a, sh, parts, tag, write_out)
+                         : merge_lists_wave<DT, kWaveMergeKeys / 64>(a, sh, parts, tag, write_out);
         first = tid;
         stride = 64u;
     } else {
