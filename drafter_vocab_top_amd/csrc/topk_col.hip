@@ -284,7 +284,7 @@ __device__ __forceinline__ bool merge_lists_wave(const ColArgs& a, ColShared& sh
 // the hardware can place them in registers as the waves start (kernarg
 // preload) instead of every workgroup reading them before its first load;
 // the rest follow in ColArgs.  Column c0 + blockIdx.y, segment blockIdx.x.
-template <class DT, int NV>
+template <class DT, int NV, bool kBigMerge>
 __global__ __launch_bounds__(kBlock) void topk_col_kernel(const void* x, int64_t ld, uint32_t V, uint32_t S,
                                                           uint32_t seg_vecs, uint32_t c0, uint32_t* tickets,
                                                           ColArgs a) {
@@ -565,7 +565,7 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(const void* x, int64_t
     };
     bool ok;
     uint32_t first, stride;
-    if ((uint32_t)a.S * k <= (uint32_t)kWaveMergeKeys) {
+    if constexpr (!kBigMerge) {
         if (wave != 0) return;
         // instantiated for the keys per lane the run needs: a larger
         // instance costs its guarded slots even where they are empty
@@ -594,11 +594,11 @@ __global__ __launch_bounds__(kBlock) void topk_col_kernel(const void* x, int64_t
 }
 
 // One launch per kColGridY columns (the grid's y size is at most 65,535).
-template <class DT, int NV>
+template <class DT, int NV, bool kBigMerge>
 hipError_t launch_nv(const ColArgs& a, hipStream_t stream) {
     for (int64_t c0 = 0; c0 < a.C; c0 += kColGridY) {
         const int64_t n = a.C - c0 < kColGridY ? a.C - c0 : kColGridY;
-        hipLaunchKernelGGL((topk_col_kernel<DT, NV>), dim3((uint32_t)a.S, (uint32_t)n), dim3(kBlock), 0, stream,
+        hipLaunchKernelGGL((topk_col_kernel<DT, NV, kBigMerge>), dim3((uint32_t)a.S, (uint32_t)n), dim3(kBlock), 0, stream,
                            a.x, a.ld, (uint32_t)a.V, (uint32_t)a.S, a.seg_vecs, (uint32_t)c0, a.tickets, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -608,11 +608,14 @@ hipError_t launch_nv(const ColArgs& a, hipStream_t stream) {
 
 template <class DT>
 hipError_t launch_dt(int nv, const ColArgs& a, hipStream_t stream) {
+    // the merge a column's last workgroup runs is chosen here, so that each
+    // kernel holds the code of one
+    const bool big = (int64_t)a.S * a.k > kWaveMergeKeys;
     switch (nv) {
-        case 2: return launch_nv<DT, 2>(a, stream);
-        case 4: return launch_nv<DT, 4>(a, stream);
-        case 8: return launch_nv<DT, 8>(a, stream);
-        case 16: return launch_nv<DT, 16>(a, stream);
+        case 2: return big ? launch_nv<DT, 2, true>(a, stream) : launch_nv<DT, 2, false>(a, stream);
+        case 4: return big ? launch_nv<DT, 4, true>(a, stream) : launch_nv<DT, 4, false>(a, stream);
+        case 8: return big ? launch_nv<DT, 8, true>(a, stream) : launch_nv<DT, 8, false>(a, stream);
+        case 16: return big ? launch_nv<DT, 16, true>(a, stream) : launch_nv<DT, 16, false>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
